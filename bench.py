@@ -1,0 +1,177 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X NVFP4 grouped GEMM.
+
+Times the HIP library on the 8-group MoE-like workload (N = 4096, K = 7168,
+M = 80, 176, 128, 72, 64, 248, 96, 160) with seeded synthetic inputs resident
+in HBM, and prints one JSON line: TFLOP/s (2*sum(MNK)/t), the roofline of the
+kernel (algorithmic bytes / measured kernel time against 8 TB/s HBM), and the
+CPU oracle timed on a bounded sample as a baseline.
+
+Cold-cache protocol: each step runs on one of R input/output replicas in
+rotation, with R chosen so the replicas together exceed twice the 256 MB
+Infinity Cache; a step never finds its operands in any cache.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+_REPO = os.path.dirname(os.path.abspath(__file__))
+if _REPO not in sys.path:
+    sys.path.insert(0, _REPO)
+
+import workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_PEAK_TFLOPS = {"fp4": 10100.0, "fp8": 5000.0, "f16": 2500.0}
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--config", type=int, default=1, help="workload index (default: the 8-group N=4096 K=7168 case)")
+    p.add_argument("--warm-cache", action="store_true", help="reuse one replica (numbers labelled warm)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--all-configs", action="store_true", help="also report every workload on stderr")
+    return p.parse_args()
+
+
+def build_replicas(groups, reps, dev):
+    import torch
+    base = []
+    for g in groups:
+        base.append([torch.from_numpy(x).to(dev) for x in (g.a, g.b, g.sfa, g.sfb)])
+    replicas = []
+    for r in range(reps):
+        rep = []
+        for g, (a, b, sa, sb) in zip(groups, base):
+            c = torch.empty((g.m, g.n), dtype=torch.float16, device=dev)
+            if r == 0:
+                rep.append((a, b, sa, sb, c))
+            else:
+                rep.append((a.clone(), b.clone(), sa.clone(), sb.clone(), c))
+        replicas.append(rep)
+    return replicas
+
+
+def time_workload(w, steps, warmup, warm_cache):
+    import torch
+    import block_scaled_fp4_group_amd as nv
+    dev = torch.device("cuda:0")
+    groups = workloads.generate(w)
+    nbytes = workloads.config_bytes(w.shapes)
+    flops = workloads.config_flops(w.shapes)
+    reps = 1 if warm_cache else max(2, -(-2 * MALL_BYTES // max(1, nbytes)) + 1)
+    replicas = build_replicas(groups, reps, dev)
+    descs = [[nv._descriptor(*g) for g in rep] for rep in replicas]
+    stream = torch.cuda.current_stream()
+    sid = stream.cuda_stream
+    for i in range(warmup):
+        nv.group_gemm_raw(descs[i % reps], sid)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        nv.group_gemm_raw(descs[i % reps], sid)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([a.elapsed_time(b) for a, b in ev])       # ms, one launch each
+    return dict(groups=groups, flops=flops, nbytes=nbytes, reps=reps, wall_ms=wall * 1e3 / steps,
+                ev_ms_mean=float(per.mean()), ev_ms_median=float(np.median(per)), ev_ms_min=float(per.min()))
+
+
+def roofline(flops, nbytes, seconds):
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    t_fp4 = flops / (MFMA_PEAK_TFLOPS["fp4"] * 1e12)
+    bound = "hbm" if t_hbm >= t_fp4 else "mfma"
+    if bound == "hbm":
+        ach = nbytes / seconds / 1e9
+        return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+    ach = flops / seconds / 1e12
+    pk = MFMA_PEAK_TFLOPS["fp4"]
+    return {"bound": "mfma", "achieved": round(ach, 1), "peak": pk, "unit": "TFLOP/s",
+            "frac": round(ach / pk, 4), "traffic": None}
+
+
+def cpu_baseline(w, groups, budget_s=20.0):
+    """The oracle as it stands, on the host cores, over whole groups of the
+    same workload taken in order until about budget_s of wall time (at least
+    one group), scaled to TFLOP/s."""
+    import oracle
+    fl, dt, used = 0.0, 0.0, 0
+    for g in groups:
+        t0 = time.perf_counter()
+        oracle.gemm_group(g.a, g.sfa, g.b, g.sfb, g.m, g.n, g.k)
+        dt += time.perf_counter() - t0
+        fl += 2.0 * g.m * g.n * g.k
+        used += 1
+        if dt >= budget_s:
+            break
+    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.max_threads(),
+            "kind": "oracle", "sample": "full fp64 oracle GEMM of %d of %d groups of %s (%.2f GFLOP), %.1f s wall"
+            % (used, len(groups), w.name, fl / 1e9, dt)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (the grouped GEMM shards by group or "
+              "by N with no exchange; multi-GPU runs are not part of it). Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    w = workloads.CONFIGS[args.config]
+    r = time_workload(w, args.steps, args.warmup, args.warm_cache)
+    kern_s = r["ev_ms_mean"] * 1e-3
+    tflops = r["flops"] / (r["wall_ms"] * 1e-3) / 1e12     # whole-job rate over the timed steps
+    line = {
+        "metric": "grouped NVFP4 GEMM TFLOP/s (2*sum(MNK)/t) and % of binding roofline, 1 MI355X",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["wall_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4 operands -> f16 mfma, f32 accumulate, f16 out",
+        "data": "synthetic (seeded, uniform E2M1 codes, E4M3FN scales 2^e(1+m/8))",
+        "config": {"workload": w.name, "groups": len(w.shapes), "shapes_mnk": [list(s) for s in w.shapes],
+                   "cache": "warm" if args.warm_cache else "cold (%d rotating replicas)" % r["reps"],
+                   "gflop": round(r["flops"] / 1e9, 3), "alg_bytes_mb": round(r["nbytes"] / 1e6, 3),
+                   "kernel_ms_mean": round(r["ev_ms_mean"], 5), "kernel_ms_median": round(r["ev_ms_median"], 5),
+                   "kernel_ms_min": round(r["ev_ms_min"], 5)},
+        "roofline": roofline(r["flops"], r["nbytes"], kern_s),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, r["groups"])
+    if args.all_configs:
+        for i, wc in enumerate(workloads.CONFIGS):
+            rc = time_workload(wc, max(10, args.steps // 2), 5, args.warm_cache)
+            s = rc["ev_ms_mean"] * 1e-3
+            rf = roofline(rc["flops"], rc["nbytes"], s)
+            print(json.dumps({"workload": wc.name, "us": round(s * 1e6, 2),
+                              "tflops": round(rc["flops"] / s / 1e12, 2),
+                              "gbs": round(rc["nbytes"] / s / 1e9, 1), "roofline": rf,
+                              "cache": "warm" if args.warm_cache else "cold"}), file=sys.stderr, flush=True)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

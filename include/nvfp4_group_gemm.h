@@ -1,0 +1,110 @@
+/*
+ * nvfp4_group_gemm.h -- C ABI of the MI355X (gfx950) NVFP4 grouped GEMM.
+ *
+ * Operation (pages "nvfp4 group gemm", kernelindex.com submissions 474067,
+ * 482269 and 496386: the header comment and MMA helper of submission 474067
+ * define E2M1 operands with one E4M3FN scale per 16 K-elements, fp32
+ * accumulation and an fp16 epilogue rounded to nearest-even; its Python entry
+ * point custom_kernel takes per-group (A, B, C) tensors, scale tensors and
+ * (M, N, K) sizes):
+ *
+ *   for each group g and every m < M_g, n < N_g:
+ *     C_g[m][n] = fp16( sum_k  e2m1(A_g[m][k]) * e4m3fn(SFA_g[m][k/16])
+ *                            * e2m1(B_g[n][k]) * e4m3fn(SFB_g[n][k/16]) )
+ *
+ * Groups are independent problems, each with its own A, B, scales and C.
+ */
+#ifndef NVFP4_GROUP_GEMM_H
+#define NVFP4_GROUP_GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define NVFP4_OK           0
+#define NVFP4_EINVAL       1  /* malformed arguments: nothing was launched            */
+#define NVFP4_EUNSUPPORTED 2  /* well-formed but outside what the kernels handle      */
+#define NVFP4_EHIP         3  /* the HIP runtime reported an error (see last_error)   */
+
+/*
+ * One group.  All pointers are DEVICE pointers owned by the caller; the
+ * library never frees or retains them.
+ *
+ *   a    E2M1 codes of A, [m][k/2] bytes, row-major.  Element k of a row sits
+ *        in byte k/2: even k in the low nibble, odd k in the high nibble.
+ *        16-byte aligned.
+ *   b    E2M1 codes of B, [n][k/2] bytes, same packing (C = A * B^T: both
+ *        operands are K-contiguous).  16-byte aligned.
+ *   sfa  E4M3FN scales of A, [m][k/16] bytes, row-major, one per 16
+ *        consecutive k.  4-byte aligned.
+ *   sfb  E4M3FN scales of B, [n][k/16] bytes, row-major.  4-byte aligned.
+ *   c    output, [m][n] IEEE fp16, row-major; written, never read.
+ *        4-byte aligned.  Must not overlap another group's c or any input.
+ *   m, n, k  problem sizes; m == 0 or n == 0 makes the group a no-op (its
+ *        pointers are not read), k == 0 writes +0 to every element of c (a, b,
+ *        sfa and sfb may then be NULL).
+ */
+typedef struct nvfp4_group {
+    const void *a;
+    const void *b;
+    const void *sfa;
+    const void *sfb;
+    void *c;
+    int32_t m;
+    int32_t n;
+    int32_t k;
+    int32_t reserved; /* must be 0 */
+} nvfp4_group_t;
+
+/*
+ * Enqueue the grouped GEMM on `stream` (a hipStream_t; NULL = the null
+ * stream) and return without synchronising.  `groups` is host memory, read
+ * only during the call.
+ *
+ * Errors (nothing is launched):
+ *   NVFP4_EINVAL        ng < 0; groups == NULL with ng > 0; m, n or k < 0;
+ *                       k % 16 != 0; c == NULL in a group with m, n > 0; a,
+ *                       b, sfa or sfb == NULL in such a group with k > 0;
+ *                       reserved != 0.
+ *   NVFP4_EUNSUPPORTED  k % 64 != 0 (the kernels read scales four at a time);
+ *                       a pointer that breaks the alignment stated above.
+ *   NVFP4_EHIP          the launch failed (message via nvfp4_last_error).
+ * The call allocates no device memory.  Calls on different streams may run
+ * concurrently.
+ */
+int nvfp4_group_gemm(const nvfp4_group_t *groups, int ng, void *stream);
+
+/*
+ * Host-only argument check: the same validation nvfp4_group_gemm performs,
+ * without touching the GPU.  Returns one of the codes above.
+ */
+int nvfp4_validate(const nvfp4_group_t *groups, int ng);
+
+/*
+ * Host-only view of the work decomposition the launch would use.  Writes up
+ * to `cap` tile records of four int32 each -- (group, first row, row count,
+ * first column) -- in the order tiles are dispatched, and returns the total
+ * number of tiles (which may exceed cap), or a negative NVFP4 code negated on
+ * invalid input.  Every output element of every non-empty group is covered
+ * by exactly one tile; a tile spans at most nvfp4_tile_cols() columns.
+ */
+int nvfp4_plan(const nvfp4_group_t *groups, int ng, int32_t *tiles, int cap);
+
+/* Largest row and column extent of one tile. */
+int nvfp4_tile_rows(void);
+int nvfp4_tile_cols(void);
+
+/*
+ * Message describing the last non-OK return on the calling thread ("" if
+ * none).  The pointer stays valid until the next call on that thread.
+ */
+const char *nvfp4_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_GROUP_GEMM_H */

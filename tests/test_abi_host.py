@@ -1,0 +1,112 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads and
+exports every entry point the header declares, argument validation returns
+the documented codes, and the tile plan covers every output exactly once."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import block_scaled_fp4_group_amd as nv
+
+REPO = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    names = set()
+    inc = os.path.join(REPO, "include")
+    for fn in os.listdir(inc):
+        if fn.endswith(".h"):
+            text = open(os.path.join(inc, fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(nvfp4_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = nv.lib()
+    names = header_functions()
+    assert "nvfp4_group_gemm" in names and len(names) >= 5
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+# fake, suitably aligned device addresses: validation never dereferences them
+A, B, SA, SB, C = 0x10000, 0x20000, 0x30000, 0x40000, 0x50000
+
+
+def G(m, n, k, **kw):
+    args = dict(a=A, b=B, sfa=SA, sfb=SB, c=C, m=m, n=n, k=k)
+    args.update(kw)
+    return nv.make_group(**args)
+
+
+@pytest.mark.parametrize("groups,code", [
+    ([G(4, 4, 64)], nv.NVFP4_OK),
+    ([], nv.NVFP4_OK),
+    ([G(-1, 4, 64)], nv.NVFP4_EINVAL),
+    ([G(4, -1, 64)], nv.NVFP4_EINVAL),
+    ([G(4, 4, -16)], nv.NVFP4_EINVAL),
+    ([G(4, 4, 24)], nv.NVFP4_EINVAL),                   # k % 16 != 0
+    ([G(4, 4, 64, c=0)], nv.NVFP4_EINVAL),
+    ([G(4, 4, 64, a=0)], nv.NVFP4_EINVAL),
+    ([G(4, 4, 64, sfb=0)], nv.NVFP4_EINVAL),
+    ([G(4, 4, 64, reserved=1)], nv.NVFP4_EINVAL),
+    ([G(0, 4, 64, a=0, b=0, c=0)], nv.NVFP4_OK),          # empty group: pointers unused
+    ([G(4, 0, 64, c=0)], nv.NVFP4_OK),
+    ([G(4, 4, 0, a=0, b=0, sfa=0, sfb=0)], nv.NVFP4_OK),  # k == 0 writes zeros
+    ([G(4, 4, 48)], nv.NVFP4_EUNSUPPORTED),             # k % 64 != 0
+    ([G(4, 4, 64, a=A + 8)], nv.NVFP4_EUNSUPPORTED),    # misaligned codes
+    ([G(4, 4, 64, sfa=SA + 2)], nv.NVFP4_EUNSUPPORTED), # misaligned scales
+    ([G(4, 4, 64, c=C + 2)], nv.NVFP4_EUNSUPPORTED),
+    ([G(4, 4, 64), G(4, 4, 24)], nv.NVFP4_EINVAL),      # error in a later group
+])
+def test_validate_codes(groups, code):
+    rc, msg = nv.validate(groups)
+    assert rc == code, msg
+    if code:
+        assert msg
+
+
+def test_validate_negative_ng_and_null():
+    lib = nv.lib()
+    assert lib.nvfp4_validate(None, -1) == nv.NVFP4_EINVAL
+    assert lib.nvfp4_validate(None, 2) == nv.NVFP4_EINVAL
+    assert lib.nvfp4_validate(None, 0) == nv.NVFP4_OK
+    assert lib.nvfp4_group_gemm(None, -3, None) == nv.NVFP4_EINVAL   # rejected before any HIP call
+    assert b"negative" in lib.nvfp4_last_error()
+
+
+def test_group_gemm_rejects_before_launch():
+    with pytest.raises(nv.Nvfp4Error) as ei:
+        nv.group_gemm_raw([G(4, 4, 24)])
+    assert ei.value.code == nv.NVFP4_EINVAL
+
+
+SHAPES = [
+    [(64, 128, 256), (128, 256, 256)],
+    [(m, 4096, 7168) for m in (80, 176, 128, 72, 64, 248, 96, 160)],
+    [(1, 8192, 7168), (17, 8192, 7168), (129, 4096, 2048), (255, 2048, 4096),
+     (512, 1024, 256), (33, 6144, 1536), (300, 3072, 7168), (8, 512, 512)],
+    [(0, 5, 64), (3, 0, 64), (1, 1, 64), (65, 129, 64), (7, 3, 0)],
+    [(16, 16, 64)] * 40,                                  # more groups than one launch holds
+]
+
+
+@pytest.mark.parametrize("shapes", SHAPES)
+def test_plan_covers_every_output_once(shapes):
+    groups = [G(m, n, k) for (m, n, k) in shapes]
+    tiles = nv.plan(groups)
+    TR, TC = nv.tile_rows(), nv.tile_cols()
+    cover = [np.zeros((m, n), np.int32) for (m, n, k) in shapes]
+    for (g, m0, rows, n0) in tiles:
+        m, n, k = shapes[g]
+        assert 0 < rows <= TR and 0 <= m0 and m0 + rows <= m and 0 <= n0 < n
+        cover[g][m0:m0 + rows, n0:min(n, n0 + TC)] += 1
+    for (m, n, k), cv in zip(shapes, cover):
+        assert (cv == 1).all()
+
+
+def test_plan_rejects_invalid():
+    with pytest.raises(nv.Nvfp4Error):
+        nv.plan([G(4, 4, 24)])

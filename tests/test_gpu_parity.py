@@ -1,0 +1,143 @@
+"""Parity of the HIP grouped GEMM with the oracle, on the GPU, through the
+C ABI.  Tolerance: |gpu - ref| <= 2e-3*|ref| + 1e-2 (tests/compare.py), and
+bit-exact where fp32 accumulation is provably exact."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests.compare import bits_equal, compare_fp16
+from tests.conftest import gpu_available
+from tests.gpu_util import log, run_gpu, sample_positions
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs an MI355X")]
+
+FINITE_E4M3 = [x for x in range(256) if x not in (0x7F, 0xFF)]
+
+
+def group(m, n, k, a=None, b=None, sfa=None, sfb=None):
+    z = lambda r, c, v=0: np.full((r, c), v, np.uint8)
+    return workloads.Group(m, n, k, z(m, k // 2) if a is None else a, z(n, k // 2) if b is None else b,
+                           z(m, k // 16, 0x38) if sfa is None else sfa,
+                           z(n, k // 16, 0x38) if sfb is None else sfb)
+
+
+def check_full(groups, label, exact=False):
+    log("gpu case: %s shapes=%s" % (label, [(g.m, g.n, g.k) for g in groups]))
+    got = run_gpu(groups)
+    r16, r64 = oracle.group_gemm(groups)
+    for i, (gbits, rb, rx) in enumerate(zip(got, r16, r64)):
+        if exact:
+            nd, where = bits_equal(gbits, rb)
+            assert nd == 0, "%s group %d: %d bit mismatches at %s" % (label, i, nd, where)
+        rep = compare_fp16(gbits, rb, rx)
+        assert rep.failures == 0, "%s group %d: %s" % (label, i, rep)
+    return got
+
+
+@pytest.mark.parametrize("side", ["a", "b"])
+def test_decode_every_code_and_scale(side):
+    """Each output isolates one (E2M1 code, E4M3FN scale) pair: bit-exact."""
+    k = 64
+    rows = 16 * len(FINITE_E4M3)
+    codes = np.zeros((rows, k // 2), np.uint8)
+    scales = np.full((rows, k // 16), 0x38, np.uint8)
+    for r in range(rows):
+        kk = (r * 7) % k                          # vary nibble position and scale block
+        codes[r, kk // 2] = (r % 16) << (4 * (kk % 2))
+        scales[r, kk // 16] = FINITE_E4M3[r // 16]
+    other = np.full((16, k // 2), 0x22, np.uint8)   # every element 1.0
+    if side == "a":
+        g = group(rows, 16, k, a=codes, sfa=scales, b=other)
+    else:
+        g = group(16, rows, k, b=codes, sfb=scales, a=other)
+    check_full([g], "decode-%s" % side, exact=True)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_small_ragged_shapes(seed):
+    rng = np.random.default_rng(seed)
+    shapes = [(1, 17, 64), (65, 130, 320), (130, 64, 576), (200, 300, 1024), (16, 1, 128), (63, 65, 2048)]
+    w = workloads.make_workload(shapes, e_range=(-8, 4), seed=seed)
+    check_full(workloads.generate(w), "ragged seed %d" % seed)
+
+
+def test_config0_full():
+    check_full(workloads.generate(workloads.CONFIGS[0]), workloads.CONFIGS[0].name)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_config_sampled(cfg):
+    w = workloads.CONFIGS[cfg]
+    groups = workloads.generate(w)
+    log("gpu case: %s (sampled parity)" % w.name)
+    got = run_gpu(groups)
+    rng = np.random.default_rng(100 + cfg)
+    for i, (g, gb) in enumerate(zip(groups, got)):
+        assert not np.isnan(gb.view(np.float16)).any(), "NaN in group %d" % i
+        rows, cols = sample_positions(g.m, g.n, 1024, rng)
+        r16, r64 = oracle.gemm_entries(g, rows, cols)
+        rep = compare_fp16(gb[rows, cols], r16, r64)
+        assert rep.failures == 0, "%s group %d: %s" % (w.name, i, rep)
+
+
+@pytest.mark.parametrize("cfg", [1, 4])
+def test_bitexact_unit_scales_full_shape(cfg):
+    """All scales 1.0: every partial sum is a multiple of 0.25 below 2^22, so
+    fp32 accumulation is exact in any order and the GPU must equal the oracle
+    bit for bit, at the full workload shapes."""
+    w = workloads.CONFIGS[cfg]
+    src = workloads.generate(w)
+    groups = [group(g.m, g.n, g.k, a=g.a, b=g.b) for g in src]
+    log("gpu case: unit scales, %s" % w.name)
+    got = run_gpu(groups)
+    rng = np.random.default_rng(200 + cfg)
+    for i, (g, gb) in enumerate(zip(groups, got)):
+        rows, cols = sample_positions(g.m, g.n, 2048, rng)
+        r16, _ = oracle.gemm_entries(g, rows, cols)
+        nd, where = bits_equal(gb[rows, cols], r16)
+        assert nd == 0, "group %d: %d mismatches" % (i, nd)
+
+
+def test_deterministic():
+    groups = workloads.generate(workloads.make_workload([(100, 200, 1024), (7, 64, 4096)], (-8, 4), 3))
+    log("gpu case: determinism")
+    a = run_gpu(groups)
+    b = run_gpu(groups)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_edge_cases():
+    rng = np.random.default_rng(4)
+    w = workloads.make_workload([(3, 5, 64), (1, 1, 64), (17, 129, 192)], (-4, 2), 4)
+    groups = workloads.generate(w)
+    groups.append(group(4, 9, 0))                                   # k == 0 -> +0
+    groups.insert(1, group(0, 8, 64))                              # empty groups are skipped
+    groups.insert(2, group(8, 0, 64))
+    log("gpu case: edge cases")
+    got = run_gpu(groups)
+    r16, r64 = oracle.group_gemm(groups)
+    for i, (gb, rb, rx) in enumerate(zip(got, r16, r64)):
+        assert gb.shape == rb.shape
+        rep = compare_fp16(gb, rb, rx)
+        assert rep.failures == 0, "group %d: %s" % (i, rep)
+    assert (got[-1] == 0).all()
+
+
+def test_many_groups_multiple_launches():
+    shapes = [(int(m), int(n), 64 * int(kk)) for m, n, kk in
+              zip(np.arange(1, 41) * 3, 16 + np.arange(40) * 5, 1 + np.arange(40) % 5)]
+    w = workloads.make_workload(shapes, (-6, 3), 5)
+    check_full(workloads.generate(w), "40 groups")
+
+
+def test_nondefault_stream():
+    import torch
+    groups = workloads.generate(workloads.make_workload([(70, 90, 512)], (-4, 2), 6))
+    log("gpu case: side stream")
+    s = torch.cuda.Stream()
+    got = run_gpu(groups, stream=s)
+    r16, r64 = oracle.group_gemm(groups)
+    assert compare_fp16(got[0], r16[0], r64[0]).failures == 0
