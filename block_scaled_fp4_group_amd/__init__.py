@@ -49,7 +49,7 @@ def lib():
         L.nvfp4_validate.restype = ctypes.c_int
         L.nvfp4_validate.argtypes = [gp, ctypes.c_int]
         L.nvfp4_plan.restype = ctypes.c_int
-        L.nvfp4_plan.argtypes = [gp, ctypes.c_int, ctypes.POINTER(ctypes.c_int32), ctypes.c_int]
+        L.nvfp4_plan.argtypes = [gp, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int32), ctypes.c_int]
         L.nvfp4_tile_rows.restype = ctypes.c_int
         L.nvfp4_tile_cols.restype = ctypes.c_int
         L.nvfp4_last_error.restype = ctypes.c_char_p
@@ -85,16 +85,18 @@ def validate(groups: Sequence[Nvfp4Group]) -> Tuple[int, str]:
     return rc, (_last_error() if rc else "")
 
 
-def plan(groups: Sequence[Nvfp4Group]) -> List[Tuple[int, int, int, int]]:
-    """Host-only tile decomposition: list of (group, m0, rows, n0)."""
+def plan(groups: Sequence[Nvfp4Group], num_workgroups: int = 256) -> List[Tuple[int, ...]]:
+    """Host-only work decomposition for a device with `num_workgroups` compute
+    units: list of segments (workgroup, group, m0, rows, n0, k_begin, k_end,
+    role); role 0 = whole tile, 1 = partial sum, 2 = finalizer."""
     arr = _array(groups)
-    n = lib().nvfp4_plan(arr, len(groups), None, 0)
+    n = lib().nvfp4_plan(arr, len(groups), num_workgroups, None, 0)
     if n < 0:
         raise Nvfp4Error(-n, _last_error())
-    buf = (ctypes.c_int32 * (4 * max(1, n)))()
-    n2 = lib().nvfp4_plan(arr, len(groups), buf, n)
+    buf = (ctypes.c_int32 * (8 * max(1, n)))()
+    n2 = lib().nvfp4_plan(arr, len(groups), num_workgroups, buf, n)
     assert n2 == n
-    return [tuple(buf[4 * i:4 * i + 4]) for i in range(n)]
+    return [tuple(buf[8 * i:8 * i + 8]) for i in range(n)]
 
 
 def tile_rows() -> int:

@@ -33,7 +33,10 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <map>
+#include <mutex>
 #include <type_traits>
+#include <utility>
 
 #include "nvfp4_group_gemm.h"
 
@@ -53,6 +56,17 @@ constexpr int kStageK = 128;         // k per pipeline stage (4 MFMA steps)
 constexpr int kFoldStages = 2;       // stages summed by MFMA before a fold (256 k)
 constexpr int kMaxGroupsPerLaunch = 32;
 
+// Work decomposition.  A group's output is cut into tiles of up to kTileM
+// rows (the rows spread evenly over the fewest tiles) by kTileN columns; K
+// is cut into stage pairs of 2 * kStageK.  The (tile, stage pair) units of a
+// launch are ordered group by group, column strip by column strip, row tile
+// by row tile, pair by pair, each weighted by an estimate of its cost, and the
+// workgroups take equal-cost contiguous ranges of that order ("stream-K").
+// A tile whose pairs fall into several ranges is finished by the workgroup
+// holding its first pair; the others leave fp32 partial sums in a workspace.
+constexpr int kCostRowBlock = 4;     // cost of one pair: kCostRowBlock per 16-row block
+constexpr int kCostFixed = 20;       //   + a fixed part (B stream and decode, A decode)
+
 struct GroupArgs {
     const uint8_t *a;
     const uint8_t *b;
@@ -62,14 +76,129 @@ struct GroupArgs {
     int32_t m, n, k;
     int32_t row_tiles;   // tiles along M
     int32_t tile_rows;   // rows per tile (multiple of 16, <= kTileM)
-    int32_t tile_begin;  // index of this group's first tile in the launch
+    int32_t col_tiles;   // tiles along N
+    int32_t npairs;      // stage pairs along K (>= 1)
+    int32_t cost_full;   // cost of one pair of a tile with tile_rows rows
+    int32_t cost_last;   // cost of one pair of the last row tile
+    int32_t pad_;
+    int64_t strip_cost;  // cost of one column strip (all row tiles, all pairs)
+    int64_t cost_begin;  // cost before this group's first unit
 };
 
 struct LaunchArgs {
     GroupArgs g[kMaxGroupsPerLaunch];
     int32_t ng;
-    int32_t total_tiles;
+    int32_t num_wg;      // workgroups of the launch
+    int64_t total_cost;
+    float *partials;     // num_wg slots of kPartialSlot bytes
+    uint32_t *flags;     // num_wg flags: slot holds this launch's partial when == epoch
+    uint32_t epoch;
 };
+
+__host__ __device__ inline int pair_cost(int nrb) { return kCostRowBlock * nrb + kCostFixed; }
+
+__host__ __device__ inline int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// First cost of workgroup w's range: pairs whose start cost lies in
+// [range_begin(w), range_begin(w + 1)) belong to w.
+__host__ __device__ inline int64_t range_begin(int64_t total, int num_wg, int w)
+{
+    return total * w / num_wg;
+}
+
+// Position of one tile and of a pair in it.
+struct TilePos {
+    int g, strip, rt;       // group, column strip, row tile
+    int pair;               // first pair of interest
+    int64_t cost_begin;     // cost of the tile's first pair
+    int pcost;              // cost of each of its pairs
+    int nrb;                // 16-row blocks of the tile
+};
+
+__host__ __device__ inline int tile_nrb(const GroupArgs &G, int rt)
+{
+    const int rows = G.m - rt * G.tile_rows < G.tile_rows ? G.m - rt * G.tile_rows : G.tile_rows;
+    return (rows + 15) >> 4;
+}
+
+__host__ __device__ inline void finish_pos(const GroupArgs &G, TilePos &p)
+{
+    const int64_t full = (int64_t)G.npairs * G.cost_full;
+    p.cost_begin = G.cost_begin + p.strip * G.strip_cost + p.rt * full;
+    p.pcost = p.rt == G.row_tiles - 1 ? G.cost_last : G.cost_full;
+    p.nrb = tile_nrb(G, p.rt);
+}
+
+// The tile holding the first pair whose start cost is >= x (g == ng: none).
+__host__ __device__ inline TilePos locate(const GroupArgs *gs, int ng, int64_t total, int64_t x)
+{
+    TilePos p{ng, 0, 0, 0, total, 1, 1};
+    if (x >= total)
+        return p;
+    int g = 0;
+    while (g + 1 < ng && gs[g + 1].cost_begin <= x)
+        ++g;
+    const GroupArgs &G = gs[g];
+    int64_t off = x - G.cost_begin;
+    p.g = g;
+    p.strip = (int)(off / G.strip_cost);
+    off -= p.strip * G.strip_cost;
+    const int64_t full = (int64_t)G.npairs * G.cost_full;
+    if (off < (int64_t)(G.row_tiles - 1) * full) {
+        p.rt = (int)(off / full);
+        off -= p.rt * full;
+        p.pair = (int)div_up(off, G.cost_full);
+    } else {
+        p.rt = G.row_tiles - 1;
+        off -= (int64_t)(G.row_tiles - 1) * full;
+        p.pair = (int)div_up(off, G.cost_last);
+    }
+    if (p.pair >= G.npairs) {        // x lies in the tile's last pair: start at the next tile
+        p.pair = 0;
+        if (++p.rt == G.row_tiles) {
+            p.rt = 0;
+            if (++p.strip == G.col_tiles) {
+                p.strip = 0;
+                if (++p.g == ng) {
+                    p.cost_begin = total;
+                    return p;
+                }
+            }
+        }
+    }
+    finish_pos(gs[p.g], p);
+    return p;
+}
+
+// The tile after p (pair 0); g == ng past the last tile.
+__host__ __device__ inline TilePos next_tile(const GroupArgs *gs, int ng, int64_t total, TilePos p)
+{
+    p.pair = 0;
+    if (++p.rt == gs[p.g].row_tiles) {
+        p.rt = 0;
+        if (++p.strip == gs[p.g].col_tiles) {
+            p.strip = 0;
+            if (++p.g == ng) {
+                p.cost_begin = total;
+                return p;
+            }
+        }
+    }
+    finish_pos(gs[p.g], p);
+    return p;
+}
+
+// Pairs [*pb, *pe) of the tile at p whose start cost lies in [lo, hi).
+__host__ __device__ inline void pairs_in(const TilePos &p, int npairs, int64_t lo, int64_t hi, int &pb, int &pe)
+{
+    int64_t b = lo <= p.cost_begin ? 0 : div_up(lo - p.cost_begin, p.pcost);
+    int64_t e = hi <= p.cost_begin ? 0 : div_up(hi - p.cost_begin, p.pcost);
+    pb = (int)(b < npairs ? b : npairs);
+    pe = (int)(e < npairs ? e : npairs);
+}
+
+// Bytes of one workgroup's partial-sum slot: [wave][row block][cb][lane] f32x4.
+constexpr uint32_t kPartialSlot = kWaves * kRowBlocks * 2u * 64u * 16u;
 
 // ---------------------------------------------------------------- device --
 
@@ -120,8 +249,8 @@ constexpr uint32_t kWindow = kWinBScales + kWaves * 2u * 256u;
 constexpr uint32_t kLdsWindows = kLdsAOps + kRing * kRawStage;
 constexpr uint32_t kLdsBytes = kLdsWindows + 2u * kWindow;
 // Loads a wave issues: 3 code loads every stage, 3 scale loads every odd
-// stage; with kRing = 3 stages in flight the count of loads issued after the
-// code loads of stage c + 1 is 9 at the start of every stage c.
+// stage (after its code loads); with kRing = 3 stages in flight, 9 loads are
+// issued after the code loads of stage c + 1 by the top of every stage c.
 constexpr int kCodeLoads = 3;
 constexpr int kWaitAfterNext = 9;
 
@@ -163,27 +292,32 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// Work of one output tile with NRB row blocks (compile-time, so the hot
-// loop has no branches).  W waves; the tile is rows [m0, m0 + rows) and
-// columns [n0, n0 + 32 W) of one group.
+// Lane index, opaque to the optimiser: addresses derived from it are formed
+// where they are used instead of being hoisted out of the persistent loop
+// (for every tile shape at once) and kept live in registers.
+__device__ __forceinline__ int lane_id()
+{
+    int l = threadIdx.x & 63;
+    asm volatile("" : "+v"(l));
+    return l;
+}
+
+// Stage pairs [pb, pe) of one output tile with NRB row blocks (compile
+// time, so the hot loop has no branches), added into `outer`.  W waves; the
+// tile is rows [m0, m0 + 16 NRB) and columns [n0, n0 + 32 W) of one group.
+// Lane (r, q) of wave w holds outer[i][cb][e] = C[m0 + 16i + 4q + e][n0 + 32w + 16cb + r].
 template <int NRB, int W>
-__device__ __forceinline__ void tile_body(const GroupArgs &G, int m0, int rows, int n0, int wave,
-                                          uint8_t *smem)
+__device__ __forceinline__ void segment(const GroupArgs &G, int m0, int n0, int wave, uint8_t *smem,
+                                        int pb, int pe, f32x4 (&outer)[NRB][2])
 {
     const int M = G.m, N = G.n, K = G.k;
-    const int lane = threadIdx.x & 63;
+    const int lane = lane_id();
     const int r = lane & 15, q = lane >> 4;
     const uint32_t row_bytes = (uint32_t)K >> 1, row_scales = (uint32_t)K >> 4;
     const int nstages = (K + kStageK - 1) / kStageK;
+    const int c_begin = 2 * pb, c_end = min(2 * pe, (nstages + 1) & ~1);
 
-    f32x4 outer[NRB][2];
-#pragma unroll
-    for (int i = 0; i < NRB; ++i)
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-            outer[i][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    if (nstages > 0) {
+    if (c_begin < c_end) {
     const i32x4 ra_codes = rsrc(G.a, (uint32_t)M * row_bytes);
     const i32x4 ra_scales = rsrc(G.sfa, (uint32_t)M * row_scales);
     const i32x4 rb_codes = rsrc(G.b, (uint32_t)N * row_bytes);
@@ -270,25 +404,28 @@ __device__ __forceinline__ void tile_body(const GroupArgs &G, int m0, int rows, 
         aop(buf, a_rb, s) = operand(codes[s], sc, s);
     };
 
-    // prologue: stages 0, 1, 2 in flight; stage 0 decoded (A to LDS, B to bf)
-    fetch_scales(0);
-    fetch_scales(1);
-    fetch_codes(0);
-    fetch_codes(1);
-    fetch_codes(2);
-    wait_vmcnt<2 * kCodeLoads>();
+    // prologue: stages c_begin .. c_begin + 2 in flight; c_begin decoded (A to
+    // LDS buffer 0, B to bf)
+    // Issue order keeps exactly kWaitAfterNext loads behind the codes of
+    // stage c + 1 at the top of every stage c, this first one included.
+    fetch_scales(c_begin >> 1);
+    fetch_codes(c_begin);
+    fetch_codes(c_begin + 1);
+    fetch_scales((c_begin >> 1) + 1);
+    fetch_codes(c_begin + 2);
+    wait_vmcnt<kWaitAfterNext>();
     {
-        const uint8_t *slot = raw_slot(0);
+        const uint8_t *slot = raw_slot(c_begin);
         uint32_t sa, sb[2];
-        read_scales(0, sa, sb);
-        const f16x2 sca = scales_of(sa, 0);
+        read_scales(c_begin, sa, sb);
+        const f16x2 sca = scales_of(sa, c_begin);
         const u32x4 ac = a_codes(slot);
 #pragma unroll
         for (int s = 0; s < 4; ++s)
             decode_a_into(ac, sca, 0, s);
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
-            const f16x2 sc = scales_of(sb[cb], 0);
+            const f16x2 sc = scales_of(sb[cb], c_begin);
             const u32x4 bc = b_codes(slot, cb);
 #pragma unroll
             for (int s = 0; s < 4; ++s)
@@ -361,17 +498,26 @@ __device__ __forceinline__ void tile_body(const GroupArgs &G, int m0, int rows, 
     // `outer`.  An odd stage count gets one extra stage whose scales are all
     // zero (its k lie past K), so the loop body has no branch.
     static_assert(kFoldStages == 2, "one fold per stage pair");
-    for (int c = 0; c < nstages; c += 2) {
+    for (int c = c_begin; c < c_end; c += 2) {
         stage(c, std::integral_constant<int, 0>{});
         stage(c + 1, std::integral_constant<int, 1>{});
         fold();
     }
-    // drain the clamped prefetches before the LDS can be reused
+    // drain the clamped prefetches before the LDS is reused
     wait_vmcnt<0>();
+    __syncthreads();
     }
+}
 
-    // epilogue: element (16i + 4q + e, 16cb + r) of this wave's 16x16 blocks
+// fp16 (round to nearest even) of the tile's sums into C, rows < m0 + rows.
+template <int NRB>
+__device__ __forceinline__ void store_tile(const GroupArgs &G, int m0, int rows, int n0, int wave,
+                                           const f32x4 (&outer)[NRB][2])
+{
+    const int lane = lane_id();
+    const int r = lane & 15, q = lane >> 4;
     _Float16 *C = G.c;
+    const int N = G.n;
 #pragma unroll
     for (int i = 0; i < NRB; ++i) {
 #pragma unroll
@@ -387,31 +533,165 @@ __device__ __forceinline__ void tile_body(const GroupArgs &G, int m0, int rows, 
     }
 }
 
+// Partial sums of split tiles.  Slot w (one per workgroup) holds the sums of
+// workgroup w's first segment in the register layout of `outer`:
+// [wave][row block][cb][lane] x f32x4.  They are written and read with
+// agent-coherent (sc1) buffer accesses, and the flag with relaxed agent-scope
+// atomics; ordering comes from waiting for the stores (vmcnt) before the flag
+// is set.  No release/acquire fence is used: on gfx950 those write back or
+// invalidate the whole L2 of the XCD, which the other workgroups streaming B
+// through that L2 would pay for.
+constexpr int kCoherent = 16;      // buffer cache-policy bits: sc1
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(const LaunchArgs &args)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(args.partials, 0, args.num_wg * (int)kPartialSlot, 0x00020000);
+}
+
+__device__ __forceinline__ int partial_base(int slot, int wave)
+{
+    return slot * (int)kPartialSlot + wave * kRowBlocks * 2 * 1024;
+}
+
+// Producer side: publish the partial sums of this workgroup's first segment.
+template <int NRB>
+__device__ __forceinline__ void publish_partial(const LaunchArgs &args, int slot, int wave,
+                                                const f32x4 (&outer)[NRB][2])
+{
+    const int lane = lane_id();
+    const __amdgpu_buffer_rsrc_t rs = partial_rsrc(args);
+    const int base = partial_base(slot, wave);
+#pragma unroll
+    for (int i = 0; i < NRB; ++i)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+            __builtin_amdgcn_raw_buffer_store_b128(outer[i][cb], rs, lane * 16, base + (i * 2 + cb) * 1024, kCoherent);
+    wait_vmcnt<0>();               // every store of this wave has reached the coherence point
+    __syncthreads();
+    if (threadIdx.x == 0)
+        __hip_atomic_store(&args.flags[slot], args.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Finalizer side: wait (bounded) for producer `slot`; true if its sums arrived.
+__device__ __forceinline__ bool await_partial(const LaunchArgs &args, int slot)
+{
+    __shared__ int ready;
+    if (threadIdx.x == 0) {
+        int ok = 0;
+        // about 0.1 s at most; a producer that never starts (not resident)
+        // makes the caller compute that part itself instead of waiting forever
+        for (int it = 0; it < (1 << 20); ++it) {
+            if (__hip_atomic_load(&args.flags[slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == args.epoch) {
+                ok = 1;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        ready = ok;
+    }
+    __syncthreads();
+    const bool ok = ready != 0;
+    __syncthreads();               // `ready` is read by everyone before the next reuse
+    return ok;
+}
+
+template <int NRB>
+__device__ __forceinline__ void add_partial(const LaunchArgs &args, int slot, int wave, f32x4 (&outer)[NRB][2])
+{
+    const int lane = lane_id();
+    const __amdgpu_buffer_rsrc_t rs = partial_rsrc(args);
+    const int base = partial_base(slot, wave);
+#pragma unroll
+    for (int i = 0; i < NRB; ++i)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+            outer[i][cb] += __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16, base + (i * 2 + cb) * 1024, kCoherent);
+}
+
+// One tile's share of this workgroup: pairs [pb, pe).  `w` is the logical
+// workgroup index, [lo, hi) its cost range.
+template <int NRB, int W>
+__device__ __forceinline__ void run_tile(const LaunchArgs &args, const TilePos &p, int pb, int pe, int w,
+                                         int wave, uint8_t *smem)
+{
+    const GroupArgs &G = args.g[p.g];
+    const int m0 = p.rt * G.tile_rows, n0 = p.strip * kTileN;
+    const int rows = min(G.tile_rows, G.m - m0);
+    f32x4 outer[NRB][2];
+#pragma unroll
+    for (int i = 0; i < NRB; ++i)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+            outer[i][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // One call site of the pipelined loop: the own segment first, then (on
+    // the finalizer) any producer part that did not arrive in time.
+    int sb = pb, se = pe, w2 = w;
+    for (;;) {
+        segment<NRB, W>(G, m0, n0, wave, smem, sb, se, outer);
+        if (pb > 0) {              // a later part of a split tile
+            publish_partial<NRB>(args, w, wave, outer);
+            return;
+        }
+        // finalizer: add the other parts of the tile in k order
+        bool recompute = false;
+        const int64_t tile_end = p.cost_begin + (int64_t)G.npairs * p.pcost;
+        while (pe < G.npairs && ++w2 < args.num_wg) {
+            const int64_t lo = range_begin(args.total_cost, args.num_wg, w2);
+            const int64_t hi = range_begin(args.total_cost, args.num_wg, w2 + 1);
+            if (lo >= tile_end)
+                break;
+            int qb, qe;
+            pairs_in(p, G.npairs, lo, hi, qb, qe);
+            if (qb >= qe)
+                continue;
+            if (await_partial(args, w2)) {
+                add_partial<NRB>(args, w2, wave, outer);
+            } else {
+                sb = qb;
+                se = qe;
+                recompute = true;
+                break;
+            }
+        }
+        if (!recompute)
+            break;
+    }
+    store_tile<NRB>(G, m0, rows, n0, wave, outer);
+}
+
 template <int W>
 __global__ __launch_bounds__(64 * W, 1) void nvfp4_group_gemm_kernel(const LaunchArgs args)
 {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
 
-    const int tile = blockIdx.x;
-    int g = 0;
-    for (int i = 1; i < args.ng; ++i)
-        if (args.g[i].tile_begin <= tile)
-            g = i;
-    const GroupArgs &G = args.g[g];
-    const int local = tile - G.tile_begin;
-    const int m0 = (local % G.row_tiles) * G.tile_rows;
-    const int n0 = (local / G.row_tiles) * (32 * W);
-    const int rows = min(G.tile_rows, G.m - m0);
+    // Logical workgroup index: consecutive ranges (which share A rows and B
+    // columns) on the same XCD when workgroups are dealt round-robin to 8 XCDs.
+    const int b = blockIdx.x, nwg = args.num_wg;
+    const int w = (nwg % 8 == 0) ? (b % 8) * (nwg / 8) + b / 8 : b;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    switch ((rows + 15) >> 4) {
-    case 1: tile_body<1, W>(G, m0, rows, n0, wave, smem); break;
-    case 2: tile_body<2, W>(G, m0, rows, n0, wave, smem); break;
-    case 3: tile_body<3, W>(G, m0, rows, n0, wave, smem); break;
-    case 4: tile_body<4, W>(G, m0, rows, n0, wave, smem); break;
-    case 5: tile_body<5, W>(G, m0, rows, n0, wave, smem); break;
-    case 6: tile_body<6, W>(G, m0, rows, n0, wave, smem); break;
-    case 7: tile_body<7, W>(G, m0, rows, n0, wave, smem); break;
-    default: tile_body<8, W>(G, m0, rows, n0, wave, smem); break;
+    const int64_t lo = range_begin(args.total_cost, nwg, w);
+    const int64_t hi = range_begin(args.total_cost, nwg, w + 1);
+
+    TilePos p = locate(args.g, args.ng, args.total_cost, lo);
+    while (p.g < args.ng) {
+        const int npairs = args.g[p.g].npairs;
+        int pb, pe;
+        pairs_in(p, npairs, lo, hi, pb, pe);
+        if (pb >= pe)
+            break;
+        switch (p.nrb) {
+        case 1: run_tile<1, W>(args, p, pb, pe, w, wave, smem); break;
+        case 2: run_tile<2, W>(args, p, pb, pe, w, wave, smem); break;
+        case 3: run_tile<3, W>(args, p, pb, pe, w, wave, smem); break;
+        case 4: run_tile<4, W>(args, p, pb, pe, w, wave, smem); break;
+        case 5: run_tile<5, W>(args, p, pb, pe, w, wave, smem); break;
+        case 6: run_tile<6, W>(args, p, pb, pe, w, wave, smem); break;
+        case 7: run_tile<7, W>(args, p, pb, pe, w, wave, smem); break;
+        default: run_tile<8, W>(args, p, pb, pe, w, wave, smem); break;
+        }
+        if (pe < npairs)
+            break;                 // the range ends inside this tile
+        p = next_tile(args.g, args.ng, args.total_cost, p);
     }
 }
 
@@ -478,25 +758,116 @@ inline void row_tiling(int m, int &tiles, int &rows_per_tile)
     tiles = ceil_div(m, rows_per_tile);
 }
 
-// Visits the tiles of all non-empty groups in dispatch order: group by group,
-// column strip by column strip, row tiles of a strip adjacent (they read the
-// same B columns).  fn(group, m0, rows, n0) is called once per tile.
-template <typename Fn>
-long long for_each_tile(const nvfp4_group_t *groups, int ng, Fn fn)
+// Fills the schedule fields of the launch's groups (non-empty groups of
+// `groups` from index *next, at most kMaxGroupsPerLaunch); returns the
+// number packed.
+int pack_launch(const nvfp4_group_t *groups, int ng, int &next, LaunchArgs &args)
 {
-    long long t = 0;
-    for (int i = 0; i < ng; ++i) {
-        const nvfp4_group_t &G = groups[i];
+    memset(&args, 0, sizeof args);
+    int n = 0;
+    int64_t cost = 0;
+    for (; next < ng && n < kMaxGroupsPerLaunch; ++next) {
+        const nvfp4_group_t &G = groups[next];
         if (G.m == 0 || G.n == 0)
             continue;
-        int rt, tr;
-        row_tiling(G.m, rt, tr);
-        const int ct = ceil_div(G.n, kTileN);
-        for (int nb = 0; nb < ct; ++nb)
-            for (int mb = 0; mb < rt; ++mb, ++t)
-                fn(i, mb * tr, (G.m - mb * tr < tr) ? G.m - mb * tr : tr, nb * kTileN);
+        GroupArgs &A = args.g[n++];
+        A.a = static_cast<const uint8_t *>(G.a);
+        A.b = static_cast<const uint8_t *>(G.b);
+        A.sfa = static_cast<const uint8_t *>(G.sfa);
+        A.sfb = static_cast<const uint8_t *>(G.sfb);
+        A.c = static_cast<_Float16 *>(G.c);
+        A.m = G.m;
+        A.n = G.n;
+        A.k = G.k;
+        row_tiling(G.m, A.row_tiles, A.tile_rows);
+        A.col_tiles = ceil_div(G.n, kTileN);
+        A.npairs = ceil_div(ceil_div(G.k, kStageK), 2);
+        if (A.npairs < 1)
+            A.npairs = 1;      // k == 0: one empty pair, the tile is still written
+        A.cost_full = pair_cost(A.tile_rows / 16);
+        A.cost_last = pair_cost(tile_nrb(A, A.row_tiles - 1));
+        A.strip_cost = (int64_t)A.npairs * ((int64_t)(A.row_tiles - 1) * A.cost_full + A.cost_last);
+        A.cost_begin = cost;
+        cost += A.strip_cost * A.col_tiles;
     }
+    args.ng = n;
+    args.total_cost = cost;
+    return n;
+}
+
+int64_t total_pairs(const LaunchArgs &args)
+{
+    int64_t t = 0;
+    for (int i = 0; i < args.ng; ++i)
+        t += (int64_t)args.g[i].row_tiles * args.g[i].col_tiles * args.g[i].npairs;
     return t;
+}
+
+int grid_for(const LaunchArgs &args, int units)
+{
+    const int64_t tp = total_pairs(args);
+    return (int)(tp < units ? tp : units);
+}
+
+// Library-owned workspace for one stream: partial-sum slots and flags.
+struct Workspace {
+    float *partials = nullptr;
+    uint32_t *flags = nullptr;
+    int slots = 0;
+    uint32_t epoch = 0;
+};
+
+std::mutex g_ws_mutex;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+int workspace_for(hipStream_t st, int device, int slots, Workspace *&out)
+{
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    Workspace &ws = g_ws[{device, st}];
+    if (ws.slots < slots) {
+        if (ws.partials) {
+            // the previous buffers may still be read by work queued on `st`
+            hipError_t e = hipStreamSynchronize(st);
+            if (e != hipSuccess)
+                return fail(NVFP4_EHIP, "stream synchronize failed: %s", hipGetErrorString(e));
+            (void)hipFree(ws.partials);
+            (void)hipFree(ws.flags);
+            ws.partials = nullptr;
+            ws.flags = nullptr;
+            ws.slots = 0;
+        }
+        hipError_t e = hipMalloc(reinterpret_cast<void **>(&ws.partials), (size_t)slots * kPartialSlot);
+        if (e == hipSuccess)
+            e = hipMalloc(reinterpret_cast<void **>(&ws.flags), (size_t)slots * sizeof(uint32_t));
+        if (e == hipSuccess)
+            e = hipMemsetAsync(ws.flags, 0, (size_t)slots * sizeof(uint32_t), st);
+        if (e != hipSuccess)
+            return fail(NVFP4_EHIP, "workspace allocation failed: %s", hipGetErrorString(e));
+        ws.slots = slots;
+        ws.epoch = 0;
+    }
+    out = &ws;
+    return NVFP4_OK;
+}
+
+int device_units(int &device, int &units)
+{
+    static std::mutex m;
+    static std::map<int, int> cache;
+    hipError_t e = hipGetDevice(&device);
+    if (e != hipSuccess)
+        return fail(NVFP4_EHIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    std::lock_guard<std::mutex> lock(m);
+    auto it = cache.find(device);
+    if (it == cache.end()) {
+        int cus = 0;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+        if (e != hipSuccess || cus <= 0)
+            return fail(NVFP4_EHIP, "cannot query the compute-unit count");
+        it = cache.emplace(device, cus).first;
+    }
+    units = it->second;
+    return NVFP4_OK;
 }
 
 }  // namespace
@@ -509,24 +880,59 @@ extern "C" int nvfp4_validate(const nvfp4_group_t *groups, int ng)
 extern "C" int nvfp4_tile_rows(void) { return kTileM; }
 extern "C" int nvfp4_tile_cols(void) { return kTileN; }
 
-extern "C" int nvfp4_plan(const nvfp4_group_t *groups, int ng, int32_t *tiles, int cap)
+extern "C" int nvfp4_plan(const nvfp4_group_t *groups, int ng, int num_workgroups, int32_t *segs, int cap)
 {
     const int rc = validate(groups, ng);
     if (rc != NVFP4_OK)
         return -rc;
-    long long t = 0;
-    const long long n = for_each_tile(groups, ng, [&](int g, int m0, int rows, int n0) {
-        if (tiles != nullptr && t < cap) {
-            tiles[4 * t + 0] = g;
-            tiles[4 * t + 1] = m0;
-            tiles[4 * t + 2] = rows;
-            tiles[4 * t + 3] = n0;
+    if (num_workgroups <= 0)
+        return -fail(NVFP4_EINVAL, "num_workgroups must be positive");
+    LaunchArgs args;
+    int next = 0, launch_first = 0;
+    long long count = 0;
+    while (next < ng) {
+        // group indices of this launch (pack_launch skips empty groups)
+        int map[kMaxGroupsPerLaunch];
+        int n = 0;
+        for (int i = launch_first; i < ng && n < kMaxGroupsPerLaunch; ++i)
+            if (groups[i].m != 0 && groups[i].n != 0)
+                map[n++] = i;
+        if (pack_launch(groups, ng, next, args) == 0)
+            break;
+        launch_first = next;
+        const int nwg = grid_for(args, num_workgroups);
+        for (int w = 0; w < nwg; ++w) {
+            const int64_t lo = range_begin(args.total_cost, nwg, w);
+            const int64_t hi = range_begin(args.total_cost, nwg, w + 1);
+            TilePos p = locate(args.g, args.ng, args.total_cost, lo);
+            while (p.g < args.ng) {
+                const GroupArgs &G = args.g[p.g];
+                int pb, pe;
+                pairs_in(p, G.npairs, lo, hi, pb, pe);
+                if (pb >= pe)
+                    break;
+                if (segs != nullptr && count < cap) {
+                    int32_t *o = segs + 8 * count;
+                    const int m0 = p.rt * G.tile_rows;
+                    o[0] = w;
+                    o[1] = map[p.g];
+                    o[2] = m0;
+                    o[3] = G.m - m0 < G.tile_rows ? G.m - m0 : G.tile_rows;
+                    o[4] = p.strip * kTileN;
+                    o[5] = 2 * kStageK * pb;
+                    o[6] = 2 * kStageK * pe;
+                    o[7] = (pb == 0 && pe == G.npairs) ? 0 : (pb > 0 ? 1 : 2);
+                }
+                ++count;
+                if (pe < G.npairs)
+                    break;
+                p = next_tile(args.g, args.ng, args.total_cost, p);
+            }
         }
-        ++t;
-    });
-    if (n > 0x7fffffffLL)
-        return -fail(NVFP4_EUNSUPPORTED, "too many tiles");
-    return (int)n;
+    }
+    if (count > 0x7fffffffLL)
+        return -fail(NVFP4_EUNSUPPORTED, "too many segments");
+    return (int)count;
 }
 
 extern "C" int nvfp4_group_gemm(const nvfp4_group_t *groups, int ng, void *stream)
@@ -535,37 +941,31 @@ extern "C" int nvfp4_group_gemm(const nvfp4_group_t *groups, int ng, void *strea
     if (rc != NVFP4_OK)
         return rc;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    int device = 0, units = 0;
     LaunchArgs args;
-    int i = 0;
-    while (i < ng) {
-        memset(&args, 0, sizeof args);
-        long long tiles = 0;
-        int n = 0;
-        for (; i < ng && n < kMaxGroupsPerLaunch; ++i) {
-            const nvfp4_group_t &G = groups[i];
-            if (G.m == 0 || G.n == 0)
-                continue;
-            GroupArgs &A = args.g[n++];
-            A.a = static_cast<const uint8_t *>(G.a);
-            A.b = static_cast<const uint8_t *>(G.b);
-            A.sfa = static_cast<const uint8_t *>(G.sfa);
-            A.sfb = static_cast<const uint8_t *>(G.sfb);
-            A.c = static_cast<_Float16 *>(G.c);
-            A.m = G.m;
-            A.n = G.n;
-            A.k = G.k;
-            row_tiling(G.m, A.row_tiles, A.tile_rows);
-            A.tile_begin = (int32_t)tiles;
-            tiles += (long long)A.row_tiles * ceil_div(G.n, kTileN);
-            if (tiles > 0x7fffffffLL)
-                return fail(NVFP4_EUNSUPPORTED, "too many tiles in one launch");
-        }
-        if (n == 0)
+    int next = 0;
+    bool queried = false;
+    while (next < ng) {
+        if (pack_launch(groups, ng, next, args) == 0)
             break;
-        args.ng = n;
-        args.total_tiles = (int32_t)tiles;
-        hipLaunchKernelGGL((nvfp4_group_gemm_kernel<kWaves>), dim3((unsigned)tiles),
-                           dim3(kThreads), 0, st, args);
+        if (!queried) {
+            const int rc2 = device_units(device, units);
+            if (rc2 != NVFP4_OK)
+                return rc2;
+            queried = true;
+        }
+        const int nwg = grid_for(args, units);
+        Workspace *ws = nullptr;
+        const int rc3 = workspace_for(st, device, units, ws);
+        if (rc3 != NVFP4_OK)
+            return rc3;
+        args.num_wg = nwg;
+        args.partials = ws->partials;
+        args.flags = ws->flags;
+        if (++ws->epoch == 0)
+            ++ws->epoch;       // 0 marks an unwritten flag
+        args.epoch = ws->epoch;
+        hipLaunchKernelGGL((nvfp4_group_gemm_kernel<kWaves>), dim3((unsigned)nwg), dim3(kThreads), 0, st, args);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return fail(NVFP4_EHIP, "kernel launch failed: %s", hipGetErrorString(e));

@@ -71,9 +71,14 @@ typedef struct nvfp4_group {
  *                       reserved != 0.
  *   NVFP4_EUNSUPPORTED  k % 64 != 0 (the kernels read scales four at a time);
  *                       a pointer that breaks the alignment stated above.
- *   NVFP4_EHIP          the launch failed (message via nvfp4_last_error).
- * The call allocates no device memory.  Calls on different streams may run
- * concurrently.
+ *   NVFP4_EHIP          a workspace allocation or the launch failed (message
+ *                       via nvfp4_last_error).
+ * Workspace: the first call on a (device, stream) pair allocates a small
+ * device workspace for that pair (partial sums of split tiles and their
+ * flags, about 128 KiB per compute unit) and keeps it for the life of the
+ * process; later calls on that pair allocate nothing.  Calls on one stream
+ * are ordered by the stream; calls on different streams use different
+ * workspaces and may run concurrently.
  */
 int nvfp4_group_gemm(const nvfp4_group_t *groups, int ng, void *stream);
 
@@ -84,14 +89,23 @@ int nvfp4_group_gemm(const nvfp4_group_t *groups, int ng, void *stream);
 int nvfp4_validate(const nvfp4_group_t *groups, int ng);
 
 /*
- * Host-only view of the work decomposition the launch would use.  Writes up
- * to `cap` tile records of four int32 each -- (group, first row, row count,
- * first column) -- in the order tiles are dispatched, and returns the total
- * number of tiles (which may exceed cap), or a negative NVFP4 code negated on
- * invalid input.  Every output element of every non-empty group is covered
- * by exactly one tile; a tile spans at most nvfp4_tile_cols() columns.
+ * Host-only view of the work decomposition a launch on a device with
+ * `num_workgroups` compute units would use.  Writes up to `cap` segment
+ * records of eight int32 each and returns the total number of segments
+ * (which may exceed cap), or a negative NVFP4 code negated on invalid input.
+ *
+ * A record is (workgroup, group, first row, row count, first column,
+ * k_begin, k_end, role): workgroup `workgroup` accumulates k in
+ * [k_begin, k_end) of the output tile rows [first row, first row + row
+ * count) x columns [first column, first column + nvfp4_tile_cols()) of
+ * `group` (clipped to n).  role 0: the segment covers the whole k range and
+ * writes C; role 1: a partial sum handed to the tile's finalizer; role 2: the
+ * finalizer, holding k_begin == 0, which adds the partial sums of the other
+ * segments of its tile and writes C.  k_end may exceed k (the last k block
+ * is padded).  Groups are launched in batches of at most 32 non-empty groups;
+ * the records of each batch follow those of the previous one.
  */
-int nvfp4_plan(const nvfp4_group_t *groups, int ng, int32_t *tiles, int cap);
+int nvfp4_plan(const nvfp4_group_t *groups, int ng, int num_workgroups, int32_t *segs, int cap);
 
 /* Largest row and column extent of one tile. */
 int nvfp4_tile_rows(void);

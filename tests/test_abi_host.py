@@ -1,6 +1,6 @@
 """Host-side checks of the C ABI (no GPU needed): the library loads and
 exports every entry point the header declares, argument validation returns
-the documented codes, and the tile plan covers every output exactly once."""
+the documented codes, and the work plan covers every output exactly once."""
 import os
 import re
 
@@ -93,18 +93,61 @@ SHAPES = [
 ]
 
 
+def _tile_key(seg):
+    return seg[1], seg[2], seg[4]
+
+
+@pytest.mark.parametrize("num_wg", [256, 1, 7, 100000])
 @pytest.mark.parametrize("shapes", SHAPES)
-def test_plan_covers_every_output_once(shapes):
+def test_plan_covers_every_output_once(shapes, num_wg):
+    """Every output element is written by exactly one segment (role 0 or 2),
+    every tile's k range is covered exactly once by its segments, and the
+    hand-off of partial sums cannot deadlock: each producer (role 1) is the
+    first segment of its workgroup, whose index is above its finalizer's."""
     groups = [G(m, n, k) for (m, n, k) in shapes]
-    tiles = nv.plan(groups)
+    segs = nv.plan(groups, num_wg)
     TR, TC = nv.tile_rows(), nv.tile_cols()
     cover = [np.zeros((m, n), np.int32) for (m, n, k) in shapes]
-    for (g, m0, rows, n0) in tiles:
+    by_tile = {}
+    first_of_wg = {}
+    for i, seg in enumerate(segs):
+        wg, g, m0, rows, n0, kb, ke, role = seg
         m, n, k = shapes[g]
-        assert 0 < rows <= TR and 0 <= m0 and m0 + rows <= m and 0 <= n0 < n
-        cover[g][m0:m0 + rows, n0:min(n, n0 + TC)] += 1
+        assert 0 <= wg < num_wg
+        assert 0 < rows <= TR and 0 <= m0 and m0 + rows <= m and 0 <= n0 < n and n0 % TC == 0
+        kpad = 256 * max(1, -(-k // 256))      # k padded to whole 256-k stage pairs
+        assert 0 <= kb < ke <= kpad and kb % 256 == 0 and ke % 256 == 0
+        first_of_wg.setdefault(wg, i)
+        by_tile.setdefault(_tile_key(seg), []).append(seg)
+        if role in (0, 2):
+            cover[g][m0:m0 + rows, n0:min(n, n0 + TC)] += 1
+            assert kb == 0
+        else:
+            assert role == 1 and kb > 0 and first_of_wg[wg] == i
     for (m, n, k), cv in zip(shapes, cover):
         assert (cv == 1).all()
+    for key, parts in by_tile.items():
+        parts.sort(key=lambda s: s[5])
+        assert parts[0][5] == 0 and all(a[6] == b[5] for a, b in zip(parts, parts[1:]))
+        k = shapes[key[0]][2]
+        assert parts[-1][6] == 256 * max(1, -(-k // 256))
+        head = parts[0]
+        assert head[7] == (0 if len(parts) == 1 else 2)
+        assert all(p[0] > head[0] for p in parts[1:])
+        # one segment per workgroup and tile
+        assert len({p[0] for p in parts}) == len(parts)
+
+
+def test_plan_balances_work():
+    """On the 8-group MoE shape every compute unit gets a near-equal share of
+    the (tile, 256-k) units, weighted by the tile height."""
+    shapes = [(m, 4096, 7168) for m in (80, 176, 128, 72, 64, 248, 96, 160)]
+    segs = nv.plan([G(*s) for s in shapes], 256)
+    load = np.zeros(256)
+    for wg, g, m0, rows, n0, kb, ke, role in segs:
+        load[wg] += (ke - kb) // 256 * (4 * (-(-rows // 16)) + 20)
+    assert (load > 0).all()
+    assert load.max() <= load.mean() + 4 * 8 + 20
 
 
 def test_plan_rejects_invalid():
