@@ -64,8 +64,13 @@ constexpr int kMaxGroupsPerLaunch = 32;
 // workgroups take equal-cost contiguous ranges of that order ("stream-K").
 // A tile whose pairs fall into several ranges is finished by the workgroup
 // holding its first pair; the others leave fp32 partial sums in a workspace.
-constexpr int kCostRowBlock = 4;     // cost of one pair: kCostRowBlock per 16-row block
-constexpr int kCostFixed = 20;       //   + a fixed part (B stream and decode, A decode)
+// Cost of one pair of a tile, in units of about 137 clocks (fitted to
+// measured segment times): kCostRowBlock per 16-row block (the MFMAs), a
+// fixed part per pair (B stream and decode, A decode, loads), and the tile's
+// own fixed work (pipeline fill and the epilogue) spread over its pairs.
+constexpr int kCostRowBlock = 4;
+constexpr int kCostFixed = 26;
+constexpr int kCostTile = 80;
 
 struct GroupArgs {
     const uint8_t *a;
@@ -95,7 +100,10 @@ struct LaunchArgs {
     uint32_t epoch;
 };
 
-__host__ __device__ inline int pair_cost(int nrb) { return kCostRowBlock * nrb + kCostFixed; }
+__host__ __device__ inline int pair_cost(int nrb, int npairs)
+{
+    return kCostRowBlock * nrb + kCostFixed + (kCostTile + npairs - 1) / npairs;
+}
 
 __host__ __device__ inline int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -510,6 +518,21 @@ __device__ __forceinline__ void segment(const GroupArgs &G, int m0, int n0, int 
 }
 
 // fp16 (round to nearest even) of the tile's sums into C, rows < m0 + rows.
+// Fast path (n % 4 == 0 and c 8-byte aligned, so every group of four
+// columns is wholly inside or outside the matrix): the four lanes of a quad
+// (r = 4j .. 4j + 3) hold rows 4q .. 4q + 3 of four consecutive columns, so a
+// 4 x 4 transpose of fp16 values across the quad (two DPP exchanges) leaves
+// each lane with four consecutive columns of one row, written as one 8-byte
+// store instead of four 2-byte ones.
+__device__ __forceinline__ uint32_t quad_swap1(uint32_t x)   // value of lane r ^ 1
+{
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t quad_swap2(uint32_t x)   // value of lane r ^ 2
+{
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);
+}
+
 template <int NRB>
 __device__ __forceinline__ void store_tile(const GroupArgs &G, int m0, int rows, int n0, int wave,
                                            const f32x4 (&outer)[NRB][2])
@@ -518,6 +541,37 @@ __device__ __forceinline__ void store_tile(const GroupArgs &G, int m0, int rows,
     const int r = lane & 15, q = lane >> 4;
     _Float16 *C = G.c;
     const int N = G.n;
+    if ((N & 3) == 0 && ((uintptr_t)C & 7) == 0) {
+        const bool odd = (r & 1) != 0, hi2 = (r & 2) != 0;
+        // this lane's row and first column after the transpose
+        const int row_in = 4 * q + 2 * (r & 1) + ((r >> 1) & 1);
+        const int col = n0 + 32 * wave + (r & ~3);
+#pragma unroll
+        for (int i = 0; i < NRB; ++i) {
+            const int row = m0 + 16 * i + row_in;
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
+                const f32x4 v = outer[i][cb];
+                const uint32_t p01 = __builtin_bit_cast(uint32_t, f16x2{(_Float16)v[0], (_Float16)v[1]});
+                const uint32_t p23 = __builtin_bit_cast(uint32_t, f16x2{(_Float16)v[2], (_Float16)v[3]});
+                // step 1: even lanes end with rows 4q, 4q+1 and odd lanes with
+                // rows 4q+2, 4q+3, each for the column pair (r & ~1, +1)
+                const uint32_t mine = odd ? p23 : p01;
+                const uint32_t recv = quad_swap1(odd ? p01 : p23);
+                const uint32_t lo = odd ? recv : mine, hi = odd ? mine : recv;
+                const uint32_t rowA = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+                const uint32_t rowB = __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+                // step 2: lanes r and r ^ 2 swap halves of their column quad
+                const uint32_t keep = hi2 ? rowB : rowA;
+                const uint32_t recv2 = quad_swap2(hi2 ? rowA : rowB);
+                const uint64_t out = hi2 ? ((uint64_t)keep << 32 | recv2) : ((uint64_t)recv2 << 32 | keep);
+                const int c0 = col + 16 * cb;
+                if (row < m0 + rows && c0 < N)
+                    *reinterpret_cast<uint64_t *>(C + (size_t)row * N + c0) = out;
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < NRB; ++i) {
 #pragma unroll
@@ -601,11 +655,20 @@ __device__ __forceinline__ void add_partial(const LaunchArgs &args, int slot, in
     const int lane = lane_id();
     const __amdgpu_buffer_rsrc_t rs = partial_rsrc(args);
     const int base = partial_base(slot, wave);
+    // all loads first (the accumulators of the hot loop are dead here, so
+    // the registers exist), then the adds: one memory latency, not 2 NRB
+    f32x4 v[NRB][2];
 #pragma unroll
     for (int i = 0; i < NRB; ++i)
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
-            outer[i][cb] += __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16, base + (i * 2 + cb) * 1024, kCoherent);
+            v[i][cb] = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16, base + (i * 2 + cb) * 1024, kCoherent);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NRB; ++i)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+            outer[i][cb] += v[i][cb];
 }
 
 // One tile's share of this workgroup: pairs [pb, pe).  `w` is the logical
@@ -784,8 +847,8 @@ int pack_launch(const nvfp4_group_t *groups, int ng, int &next, LaunchArgs &args
         A.npairs = ceil_div(ceil_div(G.k, kStageK), 2);
         if (A.npairs < 1)
             A.npairs = 1;      // k == 0: one empty pair, the tile is still written
-        A.cost_full = pair_cost(A.tile_rows / 16);
-        A.cost_last = pair_cost(tile_nrb(A, A.row_tiles - 1));
+        A.cost_full = pair_cost(A.tile_rows / 16, A.npairs);
+        A.cost_last = pair_cost(tile_nrb(A, A.row_tiles - 1), A.npairs);
         A.strip_cost = (int64_t)A.npairs * ((int64_t)(A.row_tiles - 1) * A.cost_full + A.cost_last);
         A.cost_begin = cost;
         cost += A.strip_cost * A.col_tiles;
