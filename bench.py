@@ -14,6 +14,7 @@ Infinity Cache; a step never finds its operands in any cache.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -41,7 +42,39 @@ def parse():
     p.add_argument("--warm-cache", action="store_true", help="reuse one replica (numbers labelled warm)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--all-configs", action="store_true", help="also report every workload on stderr")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                   help="run one plain device-to-device copy of BYTES first (counter calibration)")
     return p.parse_args()
+
+
+KERNEL_SOURCE = os.path.join(_REPO, "block_scaled_fp4_group_amd", "csrc", "nvfp4_group_gemm.hip")
+PROFILES = os.path.join(_REPO, "profiles")
+
+
+def kernel_source_sha():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload_name):
+    """HBM bytes per launch from the committed counter summary of this
+    workload (FETCH_SIZE + WRITE_SIZE, each scaled by the same counter's
+    reading for a plain copy of known size), or None when there is none or
+    the kernel source has changed since the counters were taken."""
+    path = os.path.join(PROFILES, "nvfp4_group_gemm_kernel_%s_traffic.txt" % workload_name)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(" "):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_source_sha():
+        return None
+    try:
+        return int(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def build_replicas(groups, reps, dev):
@@ -77,32 +110,46 @@ def time_workload(w, steps, warmup, warm_cache):
     for i in range(warmup):
         nv.group_gemm_raw(descs[i % reps], sid)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    # timed region: exactly `steps` launches, one event pair on the launch
+    # stream around all of them (per-launch events would add their own
+    # dispatch overhead to every launch)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(steps):
+        nv.group_gemm_raw(descs[i % reps], sid)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    batch_ms = e0.elapsed_time(e1) / steps
+    # distribution of single launches, measured after the timed region
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for i in range(steps):
         ev[i][0].record(stream)
         nv.group_gemm_raw(descs[i % reps], sid)
         ev[i][1].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     per = np.array([a.elapsed_time(b) for a, b in ev])       # ms, one launch each
     return dict(groups=groups, flops=flops, nbytes=nbytes, reps=reps, wall_ms=wall * 1e3 / steps,
-                ev_ms_mean=float(per.mean()), ev_ms_median=float(np.median(per)), ev_ms_min=float(per.min()))
+                ev_ms_mean=float(batch_ms), ev_ms_median=float(np.median(per)), ev_ms_min=float(per.min()))
 
 
-def roofline(flops, nbytes, seconds):
+def roofline(flops, nbytes, seconds, traffic=None):
+    """Binding roofline of the workload: HBM (algorithmic bytes at 8 TB/s) or
+    dense FP4 MFMA, whichever takes longer; achieved = algorithmic bytes (or
+    flops) per launch / mean launch time."""
     t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
     t_fp4 = flops / (MFMA_PEAK_TFLOPS["fp4"] * 1e12)
     bound = "hbm" if t_hbm >= t_fp4 else "mfma"
     if bound == "hbm":
         ach = nbytes / seconds / 1e9
         return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic}
     ach = flops / seconds / 1e12
     pk = MFMA_PEAK_TFLOPS["fp4"]
     return {"bound": "mfma", "achieved": round(ach, 1), "peak": pk, "unit": "TFLOP/s",
-            "frac": round(ach / pk, 4), "traffic": None}
+            "frac": round(ach / pk, 4), "traffic": traffic}
 
 
 def cpu_baseline(w, groups, budget_s=20.0):
@@ -136,6 +183,15 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     w = workloads.CONFIGS[args.config]
+    if args.calibrate_copy > 0:
+        n = args.calibrate_copy // 4
+        src = torch.ones(n, dtype=torch.int32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print("bench.py: calibration copy of %d bytes done" % (4 * n), file=sys.stderr, flush=True)
+        del src, dst
     r = time_workload(w, args.steps, args.warmup, args.warm_cache)
     kern_s = r["ev_ms_mean"] * 1e-3
     tflops = r["flops"] / (r["wall_ms"] * 1e-3) / 1e12     # whole-job rate over the timed steps
@@ -155,9 +211,11 @@ def main():
         "config": {"workload": w.name, "groups": len(w.shapes), "shapes_mnk": [list(s) for s in w.shapes],
                    "cache": "warm" if args.warm_cache else "cold (%d rotating replicas)" % r["reps"],
                    "gflop": round(r["flops"] / 1e9, 3), "alg_bytes_mb": round(r["nbytes"] / 1e6, 3),
-                   "kernel_ms_mean": round(r["ev_ms_mean"], 5), "kernel_ms_median": round(r["ev_ms_median"], 5),
-                   "kernel_ms_min": round(r["ev_ms_min"], 5)},
-        "roofline": roofline(r["flops"], r["nbytes"], kern_s),
+                   "kernel_ms_mean": round(r["ev_ms_mean"], 5),
+                   "single_launch_ms_median": round(r["ev_ms_median"], 5),
+                   "single_launch_ms_min": round(r["ev_ms_min"], 5)},
+        "roofline": roofline(r["flops"], r["nbytes"], kern_s,
+                             None if args.warm_cache else measured_traffic(w.name)),
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, r["groups"])
