@@ -53,7 +53,7 @@ constexpr int kTileM = 128;          // max rows of one tile (8 blocks of 16)
 constexpr int kRowBlocks = kTileM / 16;
 constexpr int kTileN = 32 * kWaves;  // columns of one tile (32 per wave)
 constexpr int kStageK = 128;         // k per pipeline stage (4 MFMA steps)
-constexpr int kFoldStages = 2;       // stages summed by MFMA before a fold (256 k)
+constexpr int kFoldStages = 4;       // stages summed by MFMA before a fold (512 k)
 constexpr int kMaxGroupsPerLaunch = 32;
 
 // Work decomposition.  A group's output is cut into tiles of up to kTileM
@@ -256,11 +256,15 @@ constexpr uint32_t kWinBScales = kWinAScales + kWaves * 256u;
 constexpr uint32_t kWindow = kWinBScales + kWaves * 2u * 256u;
 constexpr uint32_t kLdsWindows = kLdsAOps + kRing * kRawStage;
 constexpr uint32_t kLdsBytes = kLdsWindows + 2u * kWindow;
-// Loads a wave issues: 3 code loads every stage, 3 scale loads every odd
-// stage (after its code loads); with kRing = 3 stages in flight, 9 loads are
-// issued after the code loads of stage c + 1 by the top of every stage c.
+// Loads a wave issues: kCodeLoads code loads every stage, kScaleLoads
+// scale loads every odd stage (after its code loads, for the pair starting
+// three stages on).  With kRing = 3 stages in flight, at the top of every
+// stage c exactly kWaitAfterNext loads have been issued after the last load
+// that stage c + 1 needs: the codes of c + 1 when c is even, the scale
+// window of the pair starting at c + 1 when c is odd.
 constexpr int kCodeLoads = 3;
-constexpr int kWaitAfterNext = 9;
+constexpr int kScaleLoads = 2;
+constexpr int kWaitAfterNext = 2 * kCodeLoads + kScaleLoads;
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
@@ -287,6 +291,14 @@ __device__ __forceinline__ void dma16_lanes16(uint32_t lds, uint32_t voff, i32x4
 {
     uint64_t saved;
     asm volatile("s_mov_b64 %0, exec\n\ts_mov_b64 exec, 0xffff\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                 "buffer_load_dwordx4 %2, %3, %4 offen lds\n\ts_mov_b64 exec, %0"
+                 : "=&s"(saved) : "s"(lds), "v"(voff), "s"(rs), "s"(soff) : "memory", "m0");
+}
+// The same for lanes 0..31.
+__device__ __forceinline__ void dma16_lanes32(uint32_t lds, uint32_t voff, i32x4 rs, uint32_t soff)
+{
+    uint64_t saved;
+    asm volatile("s_mov_b64 %0, exec\n\ts_mov_b64 exec, 0xffffffff\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
                  "buffer_load_dwordx4 %2, %3, %4 offen lds\n\ts_mov_b64 exec, %0"
                  : "=&s"(saved) : "s"(lds), "v"(voff), "s"(rs), "s"(soff) : "memory", "m0");
 }
@@ -341,6 +353,9 @@ __device__ __forceinline__ void segment(const GroupArgs &G, int m0, int n0, int 
     const uint32_t a_voff = arow * row_bytes + 16u * q;
     const uint32_t sa_voff = arow * row_scales;
     uint32_t b_voff[2], sb_voff[2];
+    // B scale rows for one 32-lane load: lane 16 cb + r fetches column block
+    // cb's row r (lanes 32..63 are masked off)
+    const uint32_t sb_voff32 = (uint32_t)min(n0 + 32 * wave + 16 * (q & 1) + r, N - 1) * row_scales;
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
         const uint32_t col = (uint32_t)min(n0 + 32 * wave + 16 * cb + r, N - 1);
@@ -374,9 +389,7 @@ __device__ __forceinline__ void segment(const GroupArgs &G, int m0, int n0, int 
         const uint32_t sk = (uint32_t)min(w, (nstages - 1) >> 1) * (2u * kStageK / 16u);
         const uint32_t win = smem_base + kLdsWindows + (uint32_t)(w & 1) * kWindow;
         dma16_lanes16(win + kWinAScales + wave * 256u, sa_voff, ra_scales, sk);
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-            dma16_lanes16(win + kWinBScales + (wave * 2 + cb) * 256u, sb_voff[cb], rb_scales, sk);
+        dma16_lanes32(win + kWinBScales + wave * 2 * 256u, sb_voff32, rb_scales, sk);
     };
     auto raw_slot = [&](int c) -> const uint8_t * {
         return smem + kLdsAOps + (uint32_t)(c % kRing) * kRawStage;
@@ -449,9 +462,9 @@ __device__ __forceinline__ void segment(const GroupArgs &G, int m0, int n0, int 
     // after its last use), then step s of B (stage c + 1) is decoded into the
     // freed bf slot and step s of A (stage c + 1) into the other LDS buffer.
     // The last stage decodes unused data instead of branching.
-    auto stage = [&](int c, auto buf_t) {
+    auto stage = [&](int c, auto buf_t, auto first_t) {
         constexpr int kBuf = decltype(buf_t)::value;
-        constexpr bool kFirst = kBuf == 0;   // first stage after a fold: MFMA sums restart
+        constexpr bool kFirst = decltype(first_t)::value;   // first stage after a fold: MFMA sums restart
         constexpr int kNext = 1 - kBuf;
         fetch_codes(c + 3);
         if (kBuf == 1)
@@ -502,13 +515,24 @@ __device__ __forceinline__ void segment(const GroupArgs &G, int m0, int n0, int 
                 outer[i][cb] += inner[i][cb];
     };
 
-    // Stages run in pairs (LDS buffer parity) and every pair is folded into
-    // `outer`.  An odd stage count gets one extra stage whose scales are all
-    // zero (its k lie past K), so the loop body has no branch.
-    static_assert(kFoldStages == 2, "one fold per stage pair");
-    for (int c = c_begin; c < c_end; c += 2) {
-        stage(c, std::integral_constant<int, 0>{});
-        stage(c + 1, std::integral_constant<int, 1>{});
+    // Stages alternate the LDS buffer; the MFMA sums are folded into `outer`
+    // every kFoldStages stages (and after a last lone pair).  An odd stage
+    // count gets one extra stage whose scales are all zero (its k lie past
+    // K), so the loop body has no branch.
+    static_assert(kFoldStages == 4, "a fold every two stage pairs");
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    int c = c_begin;
+    for (; c + 4 <= c_end; c += 4) {
+        stage(c, B0{}, std::true_type{});
+        stage(c + 1, B1{}, std::false_type{});
+        stage(c + 2, B0{}, std::false_type{});
+        stage(c + 3, B1{}, std::false_type{});
+        fold();
+    }
+    if (c < c_end) {
+        stage(c, B0{}, std::true_type{});
+        stage(c + 1, B1{}, std::false_type{});
         fold();
     }
     // drain the clamped prefetches before the LDS is reused
