@@ -31,6 +31,7 @@
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <map>
@@ -98,6 +99,7 @@ struct LaunchArgs {
     float *partials;     // num_wg slots of kPartialSlot bytes
     uint32_t *flags;     // num_wg flags: slot holds this launch's partial when == epoch
     uint32_t epoch;
+    int32_t spin_limit;  // flag polls before a missing part is recomputed instead
 };
 
 __host__ __device__ inline int pair_cost(int nrb, int npairs)
@@ -656,9 +658,10 @@ __device__ __forceinline__ bool await_partial(const LaunchArgs &args, int slot)
     __shared__ int ready;
     if (threadIdx.x == 0) {
         int ok = 0;
-        // about 0.1 s at most; a producer that never starts (not resident)
-        // makes the caller compute that part itself instead of waiting forever
-        for (int it = 0; it < (1 << 20); ++it) {
+        // bounded (about 0.1 s by default): a producer that never starts (not
+        // resident) makes the caller compute that part itself instead of
+        // waiting forever
+        for (int it = 0; it < args.spin_limit; ++it) {
             if (__hip_atomic_load(&args.flags[slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == args.epoch) {
                 ok = 1;
                 break;
@@ -937,6 +940,15 @@ int workspace_for(hipStream_t st, int device, int slots, Workspace *&out)
     return NVFP4_OK;
 }
 
+// Flag polls before a finalizer recomputes a missing part itself.  The
+// environment variable NVFP4_SPIN_LIMIT overrides the default (0 makes every
+// split tile take the recomputation path: a test of that path).
+int spin_limit()
+{
+    const char *e = getenv("NVFP4_SPIN_LIMIT");
+    return e != nullptr ? atoi(e) : (1 << 20);
+}
+
 int device_units(int &device, int &units)
 {
     static std::mutex m;
@@ -1052,6 +1064,7 @@ extern "C" int nvfp4_group_gemm(const nvfp4_group_t *groups, int ng, void *strea
         if (++ws->epoch == 0)
             ++ws->epoch;       // 0 marks an unwritten flag
         args.epoch = ws->epoch;
+        args.spin_limit = spin_limit();
         hipLaunchKernelGGL((nvfp4_group_gemm_kernel<kWaves>), dim3((unsigned)nwg), dim3(kThreads), 0, st, args);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)

@@ -79,6 +79,11 @@ typedef struct nvfp4_group {
  * process; later calls on that pair allocate nothing.  Calls on one stream
  * are ordered by the stream; calls on different streams use different
  * workspaces and may run concurrently.
+ * Split tiles: a workgroup that finishes a tile waits (bounded) for the
+ * partial sums of the other workgroups sharing it, and computes a part that
+ * does not arrive in time itself.  The environment variable
+ * NVFP4_SPIN_LIMIT (read at each call) sets the number of polls of that
+ * wait; 0 makes every such part be recomputed (used to test that path).
  */
 int nvfp4_group_gemm(const nvfp4_group_t *groups, int ng, void *stream);
 

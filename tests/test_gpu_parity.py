@@ -141,3 +141,46 @@ def test_nondefault_stream():
     got = run_gpu(groups, stream=s)
     r16, r64 = oracle.group_gemm(groups)
     assert compare_fp16(got[0], r16[0], r64[0]).failures == 0
+
+
+SPLIT_SHAPES = [(200, 512, 2048), (72, 1024, 4096), (130, 256, 1536)]
+
+
+@pytest.mark.parametrize("spin_limit", [None, "0"])
+def test_split_tiles_full(spin_limit):
+    """Shapes small enough for the full oracle but with every tile shared by
+    several workgroups (fewer (tile, 256-k) units than compute units), so the
+    result is assembled from partial sums.  With NVFP4_SPIN_LIMIT=0 the
+    finishing workgroup never waits and computes every other part itself:
+    the recomputation path must give the same answer."""
+    import os
+    import block_scaled_fp4_group_amd as nv
+    groups = workloads.generate(workloads.make_workload(SPLIT_SHAPES, (-4, 2), 7, "split_tiles"))
+    fake = dict(a=0x10000, b=0x20000, sfa=0x30000, sfb=0x40000, c=0x50000)   # plan never dereferences
+    segs = nv.plan([nv.make_group(m=g.m, n=g.n, k=g.k, **fake) for g in groups])
+    assert any(s[7] == 2 for s in segs) and any(s[7] == 1 for s in segs)
+    old = os.environ.get("NVFP4_SPIN_LIMIT")
+    try:
+        if spin_limit is not None:
+            os.environ["NVFP4_SPIN_LIMIT"] = spin_limit
+        check_full(groups, "split tiles, spin limit %s" % spin_limit)
+    finally:
+        if old is None:
+            os.environ.pop("NVFP4_SPIN_LIMIT", None)
+        else:
+            os.environ["NVFP4_SPIN_LIMIT"] = old
+
+
+def test_config1_recomputed_parts_sampled():
+    """The 8-group K = 7168 workload with every missing part recomputed by
+    the finishing workgroup (NVFP4_SPIN_LIMIT=0), sampled against the oracle."""
+    import os
+    old = os.environ.get("NVFP4_SPIN_LIMIT")
+    os.environ["NVFP4_SPIN_LIMIT"] = "0"
+    try:
+        test_config_sampled(1)
+    finally:
+        if old is None:
+            os.environ.pop("NVFP4_SPIN_LIMIT", None)
+        else:
+            os.environ["NVFP4_SPIN_LIMIT"] = old
