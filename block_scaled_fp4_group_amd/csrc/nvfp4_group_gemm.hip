@@ -19,7 +19,10 @@
 //    (fragment-major, so every MFMA operand read is one conflict-free
 //    ds_read_b128), while each wave streams and decodes its own 32 columns of
 //    B straight from HBM into registers.  LDS stages are double-buffered and
-//    raw HBM loads are issued two stages ahead.
+//    raw HBM loads are issued two stages ahead.  The waves hand the shared
+//    A operands over through two LDS counters instead of a barrier per
+//    stage, so they drift apart and one wave's decode overlaps another's
+//    MFMAs.
 //  * Inside a 128-k stage lane (r, q) of a wave holds k = 32q + 8s + [0, 8)
 //    at MFMA step s; A and B use the same permutation of k, which leaves the
 //    sum unchanged and lets every lane read 16 contiguous bytes per row.
@@ -248,6 +251,8 @@ __device__ __forceinline__ f16x2 bcast(_Float16 x)
 // then two scale windows, each holding the scale bytes of two consecutive
 // stages (16 bytes per row, fetched by lanes 0..15, one row each):
 //   A scales [wave][16 rows] x 16 B,  B scales [wave][cb][16 rows] x 16 B
+// then two counters of decoded A halves (MFMA steps 0-1 and 2-3) that
+// order the waves' shared use of the A operand buffers.
 constexpr int kRing = 3;
 constexpr uint32_t kLdsAOps = 2u * kRowBlocks * 4u * 64u * 16u;
 constexpr uint32_t kRawACodes = 0;
@@ -257,7 +262,8 @@ constexpr uint32_t kWinAScales = 0;
 constexpr uint32_t kWinBScales = kWinAScales + kWaves * 256u;
 constexpr uint32_t kWindow = kWinBScales + kWaves * 2u * 256u;
 constexpr uint32_t kLdsWindows = kLdsAOps + kRing * kRawStage;
-constexpr uint32_t kLdsBytes = kLdsWindows + 2u * kWindow;
+constexpr uint32_t kLdsSync = kLdsWindows + 2u * kWindow;
+constexpr uint32_t kLdsBytes = kLdsSync + 16u;
 // Loads a wave issues: kCodeLoads code loads every stage, kScaleLoads
 // scale loads every odd stage (after its code loads, for the pair starting
 // three stages on).  With kRing = 3 stages in flight, at the top of every
@@ -324,6 +330,54 @@ __device__ __forceinline__ int lane_id()
     return l;
 }
 
+// The decoded A operands are the only LDS data the waves share inside the
+// stage loop (codes and scales are wave-private DMA targets).  Instead of a
+// workgroup barrier per stage, counter h (h = 0: MFMA steps 0-1, h = 1:
+// steps 2-3) counts the waves that have written their part of those steps
+// for the next stage.  Before a wave reads half h of stage c it waits until
+// every wave has written it (count >= waves * (c - first stage)); every wave
+// writes half h of stage c + 1 only after reading half h of stage c - 1,
+// which shares its buffer, so the same wait also keeps the writes of stage
+// c + 1 from overtaking a slower wave's reads of stage c - 1.  LDS performs
+// a wave's operations in issue order, so a count is added only after the
+// wave's writes.  Waves thus drift up to a stage apart, and one wave's
+// decode overlaps another's MFMAs.  The wait is bounded (a broken count
+// gives wrong sums instead of a hang).
+constexpr int kSyncSpinLimit = 1 << 14;
+// Both are single asm statements so that the hot loop stays one basic
+// block for the compiler; the LDS operations they add only make the
+// compiler's own (in-order) LDS waits more conservative.
+__device__ __forceinline__ void half_wait(uint32_t count_addr, int target)
+{
+    int v;
+    int seen, left = kSyncSpinLimit;
+    asm volatile("1:\n\t"
+                 "ds_read_b32 %0, %3\n\t"
+                 "s_waitcnt lgkmcnt(0)\n\t"
+                 "v_readfirstlane_b32 %1, %0\n\t"
+                 "s_cmp_ge_i32 %1, %4\n\t"
+                 "s_cbranch_scc1 2f\n\t"
+                 "s_sleep 1\n\t"
+                 "s_sub_i32 %2, %2, 1\n\t"
+                 "s_cmp_gt_i32 %2, 0\n\t"
+                 "s_cbranch_scc1 1b\n"
+                 "2:"
+                 : "=&v"(v), "=&s"(seen), "+s"(left)
+                 : "v"(count_addr), "s"(target)
+                 : "memory", "scc");
+}
+__device__ __forceinline__ void half_done(uint32_t count_addr, uint32_t one)
+{
+    uint64_t saved;
+    asm volatile("s_mov_b64 %0, exec\n\t"
+                 "s_mov_b64 exec, 1\n\t"
+                 "ds_add_u32 %1, %2\n\t"
+                 "s_mov_b64 exec, %0"
+                 : "=&s"(saved)
+                 : "v"(count_addr), "v"(one)
+                 : "memory");
+}
+
 // Stage pairs [pb, pe) of one output tile with NRB row blocks (compile
 // time, so the hot loop has no branches), added into `outer`.  W waves; the
 // tile is rows [m0, m0 + 16 NRB) and columns [n0, n0 + 32 W) of one group.
@@ -366,6 +420,9 @@ __device__ __forceinline__ void segment(const GroupArgs &G, int m0, int n0, int 
     }
     const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
     const uint32_t raw_base = smem_base + kLdsAOps;
+    int *sync = reinterpret_cast<int *>(smem + kLdsSync);
+    const uint32_t sync_addr = smem_base + kLdsSync;
+    const uint32_t one = 1u;
     f16x8 *lds_a = reinterpret_cast<f16x8 *>(smem);            // [2][kRowBlocks][4][64]
     auto aop = [&](int buf, int rb, int s) -> f16x8 & {
         return lds_a[((buf * kRowBlocks + rb) * 4 + s) * 64 + lane];
@@ -455,6 +512,8 @@ __device__ __forceinline__ void segment(const GroupArgs &G, int m0, int n0, int 
                 bf[cb][s] = operand(bc[s], sc, s);
         }
     }
+    if (threadIdx.x < 2)
+        sync[threadIdx.x] = 0;     // no wave counts again before this barrier
     __syncthreads();
 
     // Stage c: fetch the codes of stage c + 3 into the ring slot stage c used
@@ -463,7 +522,9 @@ __device__ __forceinline__ void segment(const GroupArgs &G, int m0, int n0, int 
     // (read from LDS; a row block's fragment for step s + 1 is read right
     // after its last use), then step s of B (stage c + 1) is decoded into the
     // freed bf slot and step s of A (stage c + 1) into the other LDS buffer.
-    // The last stage decodes unused data instead of branching.
+    // Each half of stage c's A is read only after every wave has written it
+    // (half_wait), and each written half of stage c + 1 is counted
+    // (half_done).  The last stage decodes unused data instead of branching.
     auto stage = [&](int c, auto buf_t, auto first_t) {
         constexpr int kBuf = decltype(buf_t)::value;
         constexpr bool kFirst = decltype(first_t)::value;   // first stage after a fold: MFMA sums restart
@@ -484,12 +545,16 @@ __device__ __forceinline__ void segment(const GroupArgs &G, int m0, int n0, int 
             bc_next[cb] = b_codes(nslot, cb);
         }
         const u32x4 ac_next = a_codes(nslot);
+        const int ready = __builtin_amdgcn_readfirstlane(kWaves * (c - c_begin));
+        half_wait(sync_addr, ready);
 #pragma unroll
         for (int i = 0; i < NRB; ++i)
             af[i] = aop(kBuf, i, 0);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             __builtin_amdgcn_sched_barrier(0);
+            if (s == 1)
+                half_wait(sync_addr + 4u, ready);   // step 2's fragments are read during step 1
 #pragma unroll
             for (int i = 0; i < NRB; ++i) {
 #pragma unroll
@@ -505,9 +570,10 @@ __device__ __forceinline__ void segment(const GroupArgs &G, int m0, int n0, int 
                 asm volatile("" : "+v"(bf[cb][s]));   // keep the decode inside step s
             }
             decode_a_into(ac_next, sa_next, kNext, s);
+            if (s & 1)
+                half_done(sync_addr + 4u * (s >> 1), one);
         }
         __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();
     };
     auto fold = [&]() {
 #pragma unroll
