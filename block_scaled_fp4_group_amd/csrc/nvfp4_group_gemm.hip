@@ -68,13 +68,20 @@ constexpr int kMaxGroupsPerLaunch = 32;
 // workgroups take equal-cost contiguous ranges of that order ("stream-K").
 // A tile whose pairs fall into several ranges is finished by the workgroup
 // holding its first pair; the others leave fp32 partial sums in a workspace.
-// Cost of one pair of a tile, in units of about 137 clocks (fitted to
-// measured segment times): kCostRowBlock per 16-row block (the MFMAs), a
-// fixed part per pair (B stream and decode, A decode, loads), and the tile's
-// own fixed work (pipeline fill and the epilogue) spread over its pairs.
+// Costs are in units of about 127 clocks, fitted to measured per-workgroup
+// times: a pair costs kCostRowBlock per 16-row block (the MFMAs) plus a
+// fixed part (B stream and decode, A decode, loads).  A tile's own fixed
+// work (pipeline fills, the epilogue, summing the parts of a split tile) is
+// charged partly as a head of kCostHead before its first pair and partly
+// as kCostSpread spread over its pairs, so in cost order a tile is
+// [head][pair 0][pair 1]...  Each pair belongs to the range that holds its
+// end (a range (lo, hi] of cost positions).  The split between head and
+// spread comes from a timeline model of the workgroups, in which a
+// finalizer with too little own work idles until the other parts arrive.
 constexpr int kCostRowBlock = 4;
-constexpr int kCostFixed = 26;
-constexpr int kCostTile = 80;
+constexpr int kCostFixed = 29;
+constexpr int kCostHead = 60;
+constexpr int kCostSpread = 40;
 
 struct GroupArgs {
     const uint8_t *a;
@@ -90,8 +97,8 @@ struct GroupArgs {
     int32_t cost_full;   // cost of one pair of a tile with tile_rows rows
     int32_t cost_last;   // cost of one pair of the last row tile
     int32_t pad_;
-    int64_t strip_cost;  // cost of one column strip (all row tiles, all pairs)
-    int64_t cost_begin;  // cost before this group's first unit
+    int64_t strip_cost;  // cost of one column strip (all row tiles with heads)
+    int64_t cost_begin;  // cost before this group's first tile
 };
 
 struct LaunchArgs {
@@ -107,13 +114,13 @@ struct LaunchArgs {
 
 __host__ __device__ inline int pair_cost(int nrb, int npairs)
 {
-    return kCostRowBlock * nrb + kCostFixed + (kCostTile + npairs - 1) / npairs;
+    return kCostRowBlock * nrb + kCostFixed + (kCostSpread + npairs - 1) / npairs;
 }
 
 __host__ __device__ inline int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// First cost of workgroup w's range: pairs whose start cost lies in
-// [range_begin(w), range_begin(w + 1)) belong to w.
+// Workgroup w's range is (range_begin(w), range_begin(w + 1)]: the pairs
+// whose end cost lies in it belong to w.
 __host__ __device__ inline int64_t range_begin(int64_t total, int num_wg, int w)
 {
     return total * w / num_wg;
@@ -123,7 +130,7 @@ __host__ __device__ inline int64_t range_begin(int64_t total, int num_wg, int w)
 struct TilePos {
     int g, strip, rt;       // group, column strip, row tile
     int pair;               // first pair of interest
-    int64_t cost_begin;     // cost of the tile's first pair
+    int64_t cost_begin;     // cost where the tile (its head) starts
     int pcost;              // cost of each of its pairs
     int nrb;                // 16-row blocks of the tile
 };
@@ -134,15 +141,26 @@ __host__ __device__ inline int tile_nrb(const GroupArgs &G, int rt)
     return (rows + 15) >> 4;
 }
 
+// First pair of a tile starting at cost `start` (pairs of cost pc) whose
+// end cost is > x; npairs when there is none.
+__host__ __device__ inline int first_pair_ending_after(int64_t start, int pc, int npairs, int64_t x)
+{
+    const int64_t off = x - start - kCostHead;     // pair j ends at (j + 1) pc
+    if (off < 0)
+        return 0;
+    const int64_t j = off / pc;
+    return (int)(j < npairs ? j : npairs);
+}
+
 __host__ __device__ inline void finish_pos(const GroupArgs &G, TilePos &p)
 {
-    const int64_t full = (int64_t)G.npairs * G.cost_full;
+    const int64_t full = kCostHead + (int64_t)G.npairs * G.cost_full;
     p.cost_begin = G.cost_begin + p.strip * G.strip_cost + p.rt * full;
     p.pcost = p.rt == G.row_tiles - 1 ? G.cost_last : G.cost_full;
     p.nrb = tile_nrb(G, p.rt);
 }
 
-// The tile holding the first pair whose start cost is >= x (g == ng: none).
+// The tile holding the first pair whose end cost is > x (g == ng: none).
 __host__ __device__ inline TilePos locate(const GroupArgs *gs, int ng, int64_t total, int64_t x)
 {
     TilePos p{ng, 0, 0, 0, total, 1, 1};
@@ -156,17 +174,15 @@ __host__ __device__ inline TilePos locate(const GroupArgs *gs, int ng, int64_t t
     p.g = g;
     p.strip = (int)(off / G.strip_cost);
     off -= p.strip * G.strip_cost;
-    const int64_t full = (int64_t)G.npairs * G.cost_full;
+    const int64_t full = kCostHead + (int64_t)G.npairs * G.cost_full;
     if (off < (int64_t)(G.row_tiles - 1) * full) {
         p.rt = (int)(off / full);
-        off -= p.rt * full;
-        p.pair = (int)div_up(off, G.cost_full);
+        p.pair = first_pair_ending_after(p.rt * full, G.cost_full, G.npairs, off);
     } else {
         p.rt = G.row_tiles - 1;
-        off -= (int64_t)(G.row_tiles - 1) * full;
-        p.pair = (int)div_up(off, G.cost_last);
+        p.pair = first_pair_ending_after((int64_t)(G.row_tiles - 1) * full, G.cost_last, G.npairs, off);
     }
-    if (p.pair >= G.npairs) {        // x lies in the tile's last pair: start at the next tile
+    if (p.pair >= G.npairs) {        // no pair of this tile ends after x: start at the next tile
         p.pair = 0;
         if (++p.rt == G.row_tiles) {
             p.rt = 0;
@@ -201,13 +217,11 @@ __host__ __device__ inline TilePos next_tile(const GroupArgs *gs, int ng, int64_
     return p;
 }
 
-// Pairs [*pb, *pe) of the tile at p whose start cost lies in [lo, hi).
+// Pairs [*pb, *pe) of the tile at p whose end cost lies in (lo, hi].
 __host__ __device__ inline void pairs_in(const TilePos &p, int npairs, int64_t lo, int64_t hi, int &pb, int &pe)
 {
-    int64_t b = lo <= p.cost_begin ? 0 : div_up(lo - p.cost_begin, p.pcost);
-    int64_t e = hi <= p.cost_begin ? 0 : div_up(hi - p.cost_begin, p.pcost);
-    pb = (int)(b < npairs ? b : npairs);
-    pe = (int)(e < npairs ? e : npairs);
+    pb = first_pair_ending_after(p.cost_begin, p.pcost, npairs, lo);
+    pe = first_pair_ending_after(p.cost_begin, p.pcost, npairs, hi);
 }
 
 // Bytes of one workgroup's partial-sum slot: [wave][row block][cb][lane] f32x4.
@@ -790,7 +804,7 @@ __device__ __forceinline__ void run_tile(const LaunchArgs &args, const TilePos &
         }
         // finalizer: add the other parts of the tile in k order
         bool recompute = false;
-        const int64_t tile_end = p.cost_begin + (int64_t)G.npairs * p.pcost;
+        const int64_t tile_end = p.cost_begin + kCostHead + (int64_t)G.npairs * p.pcost;
         while (pe < G.npairs && ++w2 < args.num_wg) {
             const int64_t lo = range_begin(args.total_cost, args.num_wg, w2);
             const int64_t hi = range_begin(args.total_cost, args.num_wg, w2 + 1);
@@ -942,7 +956,8 @@ int pack_launch(const nvfp4_group_t *groups, int ng, int &next, LaunchArgs &args
             A.npairs = 1;      // k == 0: one empty pair, the tile is still written
         A.cost_full = pair_cost(A.tile_rows / 16, A.npairs);
         A.cost_last = pair_cost(tile_nrb(A, A.row_tiles - 1), A.npairs);
-        A.strip_cost = (int64_t)A.npairs * ((int64_t)(A.row_tiles - 1) * A.cost_full + A.cost_last);
+        A.strip_cost = (int64_t)A.row_tiles * kCostHead +
+                       (int64_t)A.npairs * ((int64_t)(A.row_tiles - 1) * A.cost_full + A.cost_last);
         A.cost_begin = cost;
         cost += A.strip_cost * A.col_tiles;
     }

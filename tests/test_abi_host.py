@@ -139,10 +139,11 @@ def test_plan_covers_every_output_once(shapes, num_wg):
 
 
 def test_plan_balances_work():
-    """Every compute unit gets a near-equal share of the (tile, 256-k) units,
-    each weighted by the scheduler's cost: 4 per 16-row block, 26 per pair and
-    80 per tile spread over its pairs.  No share exceeds the mean by more than
-    the cost of one pair."""
+    """Every compute unit gets a near-equal share of the work, in the
+    scheduler's cost units: per pair of a tile 4 per 16-row block, 29, and
+    40 spread over the tile's pairs, plus 60 for a tile's head (charged to
+    the unit that takes its first pair).  No share exceeds the mean by more
+    than the largest such unit."""
     for shapes in ([(m, 4096, 7168) for m in (80, 176, 128, 72, 64, 248, 96, 160)],
                    [(1, 8192, 7168), (17, 8192, 7168), (129, 4096, 2048), (255, 2048, 4096),
                     (512, 1024, 256), (33, 6144, 1536), (300, 3072, 7168), (8, 512, 512)]):
@@ -151,9 +152,9 @@ def test_plan_balances_work():
         worst_pair = 0
         for wg, g, m0, rows, n0, kb, ke, role in segs:
             npairs = max(1, -(-shapes[g][2] // 256))
-            pc = 4 * (-(-rows // 16)) + 26 + -(-80 // npairs)
-            worst_pair = max(worst_pair, pc)
-            load[wg] += (ke - kb) // 256 * pc
+            pc = 4 * (-(-rows // 16)) + 29 + -(-40 // npairs)
+            worst_pair = max(worst_pair, pc + 60)
+            load[wg] += (ke - kb) // 256 * pc + (60 if kb == 0 else 0)
         assert (load > 0).all()
         assert load.max() <= load.mean() + worst_pair
 
