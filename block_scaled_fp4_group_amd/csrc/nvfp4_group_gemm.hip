@@ -103,6 +103,9 @@ struct GroupArgs {
 
 struct LaunchArgs {
     GroupArgs g[kMaxGroupsPerLaunch];
+    // g[i].cost_begin again, contiguous (INT64_MAX past the last group), so
+    // that finding a cost's group is one batch of independent loads
+    int64_t group_begin[kMaxGroupsPerLaunch];
     int32_t ng;
     int32_t num_wg;      // workgroups of the launch
     int64_t total_cost;
@@ -161,14 +164,18 @@ __host__ __device__ inline void finish_pos(const GroupArgs &G, TilePos &p)
 }
 
 // The tile holding the first pair whose end cost is > x (g == ng: none).
-__host__ __device__ inline TilePos locate(const GroupArgs *gs, int ng, int64_t total, int64_t x)
+__host__ __device__ inline TilePos locate(const LaunchArgs &args, int64_t x)
 {
+    const GroupArgs *gs = args.g;
+    const int ng = args.ng;
+    const int64_t total = args.total_cost;
     TilePos p{ng, 0, 0, 0, total, 1, 1};
     if (x >= total)
         return p;
     int g = 0;
-    while (g + 1 < ng && gs[g + 1].cost_begin <= x)
-        ++g;
+#pragma unroll
+    for (int i = 1; i < kMaxGroupsPerLaunch; ++i)
+        g += args.group_begin[i] <= x ? 1 : 0;
     const GroupArgs &G = gs[g];
     int64_t off = x - G.cost_begin;
     p.g = g;
@@ -842,7 +849,7 @@ __global__ __launch_bounds__(64 * W, 1) void nvfp4_group_gemm_kernel(const Launc
     const int64_t lo = range_begin(args.total_cost, nwg, w);
     const int64_t hi = range_begin(args.total_cost, nwg, w + 1);
 
-    TilePos p = locate(args.g, args.ng, args.total_cost, lo);
+    TilePos p = locate(args, lo);
     while (p.g < args.ng) {
         const int npairs = args.g[p.g].npairs;
         int pb, pe;
@@ -959,8 +966,11 @@ int pack_launch(const nvfp4_group_t *groups, int ng, int &next, LaunchArgs &args
         A.strip_cost = (int64_t)A.row_tiles * kCostHead +
                        (int64_t)A.npairs * ((int64_t)(A.row_tiles - 1) * A.cost_full + A.cost_last);
         A.cost_begin = cost;
+        args.group_begin[n - 1] = cost;
         cost += A.strip_cost * A.col_tiles;
     }
+    for (int i = n; i < kMaxGroupsPerLaunch; ++i)
+        args.group_begin[i] = INT64_MAX;
     args.ng = n;
     args.total_cost = cost;
     return n;
@@ -1084,7 +1094,7 @@ extern "C" int nvfp4_plan(const nvfp4_group_t *groups, int ng, int num_workgroup
         for (int w = 0; w < nwg; ++w) {
             const int64_t lo = range_begin(args.total_cost, nwg, w);
             const int64_t hi = range_begin(args.total_cost, nwg, w + 1);
-            TilePos p = locate(args.g, args.ng, args.total_cost, lo);
+            TilePos p = locate(args, lo);
             while (p.g < args.ng) {
                 const GroupArgs &G = args.g[p.g];
                 int pb, pe;
