@@ -38,6 +38,7 @@
 #include <string.h>
 
 #include <map>
+#include <vector>
 #include <mutex>
 #include <type_traits>
 #include <utility>
@@ -59,25 +60,23 @@ constexpr int kTileN = 32 * kWaves;  // columns of one tile (32 per wave)
 constexpr int kStageK = 128;         // k per pipeline stage (4 MFMA steps)
 constexpr int kFoldStages = 4;       // stages summed by MFMA before a fold (512 k)
 constexpr int kMaxGroupsPerLaunch = 32;
+constexpr int kMaxWorkgroups = 256;   // workgroups of one launch (one per CU on MI355X)
 
 // Work decomposition.  A group's output is cut into tiles of up to kTileM
 // rows (the rows spread evenly over the fewest tiles) by kTileN columns; K
 // is cut into stage pairs of 2 * kStageK.  The (tile, stage pair) units of a
 // launch are ordered group by group, column strip by column strip, row tile
-// by row tile, pair by pair, each weighted by an estimate of its cost, and the
-// workgroups take equal-cost contiguous ranges of that order ("stream-K").
-// A tile whose pairs fall into several ranges is finished by the workgroup
-// holding its first pair; the others leave fp32 partial sums in a workspace.
-// Costs are in units of about 127 clocks, fitted to measured per-workgroup
-// times: a pair costs kCostRowBlock per 16-row block (the MFMAs) plus a
-// fixed part (B stream and decode, A decode, loads).  A tile's own fixed
-// work (pipeline fills, the epilogue, summing the parts of a split tile) is
-// charged partly as a head of kCostHead before its first pair and partly
-// as kCostSpread spread over its pairs, so in cost order a tile is
-// [head][pair 0][pair 1]...  Each pair belongs to the range that holds its
-// end (a range (lo, hi] of cost positions).  The split between head and
-// spread comes from a timeline model of the workgroups, in which a
-// finalizer with too little own work idles until the other parts arrive.
+// by row tile, pair by pair, and every workgroup takes one contiguous range
+// of that order ("stream-K").  The host chooses the ranges (plan_cuts) by
+// balancing a clock model of each workgroup.  A tile whose pairs fall into
+// several ranges is finished by the workgroup holding its first pair; the
+// others leave fp32 partial sums in a workspace.
+// Positions in the order are cost coordinates: a tile is [head][pair 0]
+// [pair 1]..., a pair of a tile with nrb row blocks spans pair_cost(nrb,
+// npairs) units and a head kCostHead, and a pair belongs to the range
+// (lo, hi] that holds its end.  The host places cuts on pair ends, so these
+// weights only fix the coordinates (their values were an earlier cost
+// estimate, in units of about 127 clocks).
 constexpr int kCostRowBlock = 4;
 constexpr int kCostFixed = 29;
 constexpr int kCostHead = 60;
@@ -113,6 +112,10 @@ struct LaunchArgs {
     uint32_t *flags;     // num_wg flags: slot holds this launch's partial when == epoch
     uint32_t epoch;
     int32_t spin_limit;  // flag polls before a missing part is recomputed instead
+    // Workgroup w's range is the cost interval (cut[w], cut[w + 1]]: the
+    // pairs whose end cost lies in it belong to w (cut[0] = 0, cut[num_wg] =
+    // total_cost, non-decreasing; chosen on the host)
+    int64_t cut[kMaxWorkgroups + 1];
 };
 
 __host__ __device__ inline int pair_cost(int nrb, int npairs)
@@ -121,13 +124,6 @@ __host__ __device__ inline int pair_cost(int nrb, int npairs)
 }
 
 __host__ __device__ inline int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
-
-// Workgroup w's range is (range_begin(w), range_begin(w + 1)]: the pairs
-// whose end cost lies in it belong to w.
-__host__ __device__ inline int64_t range_begin(int64_t total, int num_wg, int w)
-{
-    return total * w / num_wg;
-}
 
 // Position of one tile and of a pair in it.
 struct TilePos {
@@ -813,8 +809,8 @@ __device__ __forceinline__ void run_tile(const LaunchArgs &args, const TilePos &
         bool recompute = false;
         const int64_t tile_end = p.cost_begin + kCostHead + (int64_t)G.npairs * p.pcost;
         while (pe < G.npairs && ++w2 < args.num_wg) {
-            const int64_t lo = range_begin(args.total_cost, args.num_wg, w2);
-            const int64_t hi = range_begin(args.total_cost, args.num_wg, w2 + 1);
+            const int64_t lo = args.cut[w2];
+            const int64_t hi = args.cut[w2 + 1];
             if (lo >= tile_end)
                 break;
             int qb, qe;
@@ -846,8 +842,8 @@ __global__ __launch_bounds__(64 * W, 1) void nvfp4_group_gemm_kernel(const Launc
     const int b = blockIdx.x, nwg = args.num_wg;
     const int w = (nwg % 8 == 0) ? (b % 8) * (nwg / 8) + b / 8 : b;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t lo = range_begin(args.total_cost, nwg, w);
-    const int64_t hi = range_begin(args.total_cost, nwg, w + 1);
+    const int64_t lo = args.cut[w];
+    const int64_t hi = args.cut[w + 1];
 
     TilePos p = locate(args, lo);
     while (p.g < args.ng) {
@@ -987,7 +983,142 @@ int64_t total_pairs(const LaunchArgs &args)
 int grid_for(const LaunchArgs &args, int units)
 {
     const int64_t tp = total_pairs(args);
-    return (int)(tp < units ? tp : units);
+    int64_t g = tp < units ? tp : units;
+    if (g > kMaxWorkgroups)
+        g = kMaxWorkgroups;
+    return (int)g;
+}
+
+// Partition of a launch's (tile, pair) sequence among num_wg workgroups.
+// A greedy fill against a target makespan, binary-searched: each workgroup
+// takes pairs in order while its modelled time stays within the target.
+// The model (clocks, fitted to per-workgroup timestamps of this kernel on
+// MI355X) charges a workgroup its start-up, a pipeline fill per segment (the
+// first one dearer), the pairs (a fixed part plus a part per 16-row block),
+// and each segment's epilogue:
+//  * a whole tile: its store;
+//  * the later part of a split tile (its workgroup's first segment): the
+//    publish of its partial sums;
+//  * the first part (the finalizer's): the store plus one sum per other
+//    part (one other part if the next workgroup can take the rest of the
+//    tile, else two);
+//  * a middle part (a workgroup whose whole range lies inside the tile): its
+//    publish must leave the finalizer time for two sums and the store.
+constexpr double kClkStart = 7000;
+constexpr double kClkFillFirst = 14200;
+constexpr double kClkFillNext = 9400;
+constexpr double kClkPair = 2440;
+constexpr double kClkPairRowBlock = 562;
+constexpr double kClkPublish = 3300;
+constexpr double kClkStore = 5000;
+constexpr double kClkAdd = 3700;
+
+// One tile of the launch for the partition: where it starts in cost order,
+// its pair cost there, and its pairs' modelled clocks.
+struct PlanTile {
+    int64_t cost_begin;
+    int32_t pcost, npairs;
+    double pair_clk;
+};
+
+bool greedy_cuts(const std::vector<PlanTile> &tiles, int nwg, int64_t total, double tmax, int64_t *cut)
+{
+    int w = 0;
+    double cur = kClkStart;
+    bool fresh = true;             // workgroup w has no segment yet
+    cut[0] = 0;
+    for (const PlanTile &t : tiles) {
+        const int npairs = t.npairs;
+        const double pc = t.pair_clk;
+        int j = 0;
+        while (j < npairs) {
+            const double base = cur + (fresh ? kClkFillFirst : kClkFillNext);
+            const int rest = npairs - j;
+            const double epi_full = j == 0 ? kClkStore : kClkPublish;
+            if (base + rest * pc + epi_full <= tmax) {   // the rest of the tile fits
+                cur = base + rest * pc + epi_full;
+                fresh = false;
+                break;
+            }
+            // pairs this workgroup can take before its range ends in the tile
+            auto take = [&](double epi) {
+                const double fit = (tmax - base - epi) / pc;
+                return fit < 0 ? 0 : (fit > rest - 1 ? rest - 1 : (int)fit);
+            };
+            auto next_takes_rest = [&](int r) {
+                return kClkStart + kClkFillFirst + r * pc + kClkPublish <= tmax;
+            };
+            int k;
+            if (j == 0) {
+                k = take(kClkStore + kClkAdd);
+                if (!(k >= 1 && next_takes_rest(rest - k)))
+                    k = take(kClkStore + 2 * kClkAdd);
+            } else {
+                k = take(kClkPublish + kClkStore + 2 * kClkAdd);
+            }
+            j += k;
+            // workgroup w ends with pair j - 1 of this tile (or before the tile)
+            if (++w >= nwg)
+                return false;
+            cut[w] = j == 0 ? t.cost_begin : t.cost_begin + kCostHead + (int64_t)j * t.pcost;
+            cur = kClkStart;
+            fresh = true;
+        }
+    }
+    for (int i = w + 1; i <= nwg; ++i)
+        cut[i] = total;
+    return true;
+}
+
+// The last partition computed on this host thread, reused while the
+// launch's shapes and workgroup count stay the same.
+struct CutCache {
+    int nwg = -1, ng = 0;
+    int32_t mnk[kMaxGroupsPerLaunch][3];
+    int64_t cut[kMaxWorkgroups + 1];
+};
+thread_local CutCache g_cut_cache;
+
+void plan_cuts(LaunchArgs &a, int nwg)
+{
+    CutCache &cc = g_cut_cache;
+    bool same = cc.nwg == nwg && cc.ng == a.ng;
+    for (int i = 0; same && i < a.ng; ++i)
+        same = cc.mnk[i][0] == a.g[i].m && cc.mnk[i][1] == a.g[i].n && cc.mnk[i][2] == a.g[i].k;
+    if (same) {
+        memcpy(a.cut, cc.cut, sizeof(int64_t) * (nwg + 1));
+        return;
+    }
+    std::vector<PlanTile> tiles;
+    double work = 0, biggest = 0;
+    for (TilePos p = locate(a, 0); p.g < a.ng; p = next_tile(a.g, a.ng, a.total_cost, p)) {
+        const PlanTile t{p.cost_begin, p.pcost, a.g[p.g].npairs, kClkPair + kClkPairRowBlock * p.nrb};
+        const double tile = kClkFillFirst + kClkStore + 2 * kClkAdd + t.npairs * t.pair_clk;
+        work += t.npairs * t.pair_clk;
+        biggest = tile > biggest ? tile : biggest;
+        tiles.push_back(t);
+    }
+    // the makespan lies between the average work and that plus a whole tile
+    double lo = kClkStart + work / nwg;
+    double hi = lo + biggest + kClkFillFirst + kClkStore + 2 * kClkAdd;
+    while (!greedy_cuts(tiles, nwg, a.total_cost, hi, a.cut))
+        hi *= 2;
+    for (int it = 0; it < 24 && hi - lo > 64.0; ++it) {
+        const double mid = 0.5 * (lo + hi);
+        if (greedy_cuts(tiles, nwg, a.total_cost, mid, a.cut))
+            hi = mid;
+        else
+            lo = mid;
+    }
+    greedy_cuts(tiles, nwg, a.total_cost, hi, a.cut);
+    cc.nwg = nwg;
+    cc.ng = a.ng;
+    for (int i = 0; i < a.ng; ++i) {
+        cc.mnk[i][0] = a.g[i].m;
+        cc.mnk[i][1] = a.g[i].n;
+        cc.mnk[i][2] = a.g[i].k;
+    }
+    memcpy(cc.cut, a.cut, sizeof(int64_t) * (nwg + 1));
 }
 
 // Library-owned workspace for one stream: partial-sum slots and flags.
@@ -1091,9 +1222,10 @@ extern "C" int nvfp4_plan(const nvfp4_group_t *groups, int ng, int num_workgroup
             break;
         launch_first = next;
         const int nwg = grid_for(args, num_workgroups);
+        plan_cuts(args, nwg);
         for (int w = 0; w < nwg; ++w) {
-            const int64_t lo = range_begin(args.total_cost, nwg, w);
-            const int64_t hi = range_begin(args.total_cost, nwg, w + 1);
+            const int64_t lo = args.cut[w];
+            const int64_t hi = args.cut[w + 1];
             TilePos p = locate(args, lo);
             while (p.g < args.ng) {
                 const GroupArgs &G = args.g[p.g];
@@ -1150,6 +1282,7 @@ extern "C" int nvfp4_group_gemm(const nvfp4_group_t *groups, int ng, void *strea
         if (rc3 != NVFP4_OK)
             return rc3;
         args.num_wg = nwg;
+        plan_cuts(args, nwg);
         args.partials = ws->partials;
         args.flags = ws->flags;
         if (++ws->epoch == 0)

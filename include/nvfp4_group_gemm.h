@@ -84,6 +84,10 @@ typedef struct nvfp4_group {
  * does not arrive in time itself.  The environment variable
  * NVFP4_SPIN_LIMIT (read at each call) sets the number of polls of that
  * wait; 0 makes every such part be recomputed (used to test that path).
+ * Host cost: each launch of up to 32 groups uses at most min(compute units,
+ * 256) workgroups, whose work ranges the host balances with a timing model
+ * of the kernel (tens of microseconds); the last result is reused, per host
+ * thread, while the groups' sizes stay the same.
  */
 int nvfp4_group_gemm(const nvfp4_group_t *groups, int ng, void *stream);
 
