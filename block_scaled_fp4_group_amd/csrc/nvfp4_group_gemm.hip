@@ -994,8 +994,9 @@ int grid_for(const LaunchArgs &args, int units)
 // takes pairs in order while its modelled time stays within the target.
 // The model (clocks, fitted to per-workgroup timestamps of this kernel on
 // MI355X) charges a workgroup its start-up, a pipeline fill per segment (the
-// first one dearer), the pairs (a fixed part plus a part per 16-row block),
-// and each segment's epilogue:
+// first one dearer), the pairs (measured per tile height: a pair of a short
+// tile is bound by streaming B, not by its MFMAs), and each segment's
+// epilogue:
 //  * a whole tile: its store;
 //  * the later part of a split tile (its workgroup's first segment): the
 //    publish of its partial sums;
@@ -1007,11 +1008,10 @@ int grid_for(const LaunchArgs &args, int units)
 constexpr double kClkStart = 7000;
 constexpr double kClkFillFirst = 14200;
 constexpr double kClkFillNext = 9400;
-constexpr double kClkPair = 2440;
-constexpr double kClkPairRowBlock = 562;
+constexpr double kClkPair[kRowBlocks + 1] = {0, 4212, 4634, 4648, 4880, 5305, 5622, 6141, 6988};
 constexpr double kClkPublish = 3300;
 constexpr double kClkStore = 5000;
-constexpr double kClkAdd = 3700;
+constexpr double kClkAdd = 4000;
 
 // One tile of the launch for the partition: where it starts in cost order,
 // its pair cost there, and its pairs' modelled clocks.
@@ -1092,7 +1092,7 @@ void plan_cuts(LaunchArgs &a, int nwg)
     std::vector<PlanTile> tiles;
     double work = 0, biggest = 0;
     for (TilePos p = locate(a, 0); p.g < a.ng; p = next_tile(a.g, a.ng, a.total_cost, p)) {
-        const PlanTile t{p.cost_begin, p.pcost, a.g[p.g].npairs, kClkPair + kClkPairRowBlock * p.nrb};
+        const PlanTile t{p.cost_begin, p.pcost, a.g[p.g].npairs, kClkPair[p.nrb]};
         const double tile = kClkFillFirst + kClkStore + 2 * kClkAdd + t.npairs * t.pair_clk;
         work += t.npairs * t.pair_clk;
         biggest = tile > biggest ? tile : biggest;
