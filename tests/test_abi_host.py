@@ -175,3 +175,20 @@ def test_plan_balances_work():
 def test_plan_rejects_invalid():
     with pytest.raises(nv.Nvfp4Error):
         nv.plan([G(4, 4, 24)])
+
+def test_plan_cache_keys_on_sizes():
+    """The host keeps the last partition per thread; a plan for other sizes
+    or another unit count in between must not leak into the next one."""
+    a = [(m, 4096, 7168) for m in (80, 176, 128, 72, 64, 248, 96, 160)]
+    b = [(1, 8192, 7168), (17, 8192, 7168), (129, 4096, 2048), (255, 2048, 4096)]
+    c = [(m, 4096, 7168) for m in (80, 176, 128, 72, 64, 248, 96, 161)]   # one size differs
+    first = nv.plan([G(*s) for s in a], 256)
+    other = nv.plan([G(*s) for s in b], 256)
+    again = nv.plan([G(*s) for s in a], 256)
+    assert first == again and first != other
+    fewer = nv.plan([G(*s) for s in a], 200)
+    assert max(seg[0] for seg in fewer) < 200
+    assert nv.plan([G(*s) for s in a], 256) == first
+    near = nv.plan([G(*s) for s in c], 256)
+    assert near != first
+    assert nv.plan([G(*s) for s in c], 256) == near
