@@ -116,6 +116,8 @@ struct LaunchArgs {
     // pairs whose end cost lies in it belong to w (cut[0] = 0, cut[num_wg] =
     // total_cost, non-decreasing; chosen on the host)
     int64_t cut[kMaxWorkgroups + 1];
+    // workgroup w's first tile and pair (pack_start), found by the host
+    uint64_t start[kMaxWorkgroups];
 };
 
 __host__ __device__ inline int pair_cost(int nrb, int npairs)
@@ -217,6 +219,26 @@ __host__ __device__ inline TilePos next_tile(const GroupArgs *gs, int ng, int64_
         }
     }
     finish_pos(gs[p.g], p);
+    return p;
+}
+
+// A tile position packed into 64 bits: pair [0, 20), row tile [20, 38),
+// column strip [38, 58), group [58, 64) (63: no tile).
+__host__ __device__ inline uint64_t pack_start(const TilePos &p, int ng)
+{
+    if (p.g >= ng)
+        return 63ull << 58;
+    return (uint64_t)p.pair | (uint64_t)p.rt << 20 | (uint64_t)p.strip << 38 | (uint64_t)p.g << 58;
+}
+
+__host__ __device__ inline TilePos unpack_start(const LaunchArgs &args, uint64_t v)
+{
+    TilePos p{(int)(v >> 58), (int)((v >> 38) & 0xFFFFF), (int)((v >> 20) & 0x3FFFF), (int)(v & 0xFFFFF),
+              args.total_cost, 1, 1};
+    if (p.g < args.ng)
+        finish_pos(args.g[p.g], p);
+    else
+        p.g = args.ng;
     return p;
 }
 
@@ -845,7 +867,7 @@ __global__ __launch_bounds__(64 * W, 1) void nvfp4_group_gemm_kernel(const Launc
     const int64_t lo = args.cut[w];
     const int64_t hi = args.cut[w + 1];
 
-    TilePos p = locate(args, lo);
+    TilePos p = unpack_start(args, args.start[w]);
     while (p.g < args.ng) {
         const int npairs = args.g[p.g].npairs;
         int pb, pe;
@@ -1076,6 +1098,7 @@ struct CutCache {
     int nwg = -1, ng = 0;
     int32_t mnk[kMaxGroupsPerLaunch][3];
     int64_t cut[kMaxWorkgroups + 1];
+    uint64_t start[kMaxWorkgroups];
 };
 thread_local CutCache g_cut_cache;
 
@@ -1087,6 +1110,7 @@ void plan_cuts(LaunchArgs &a, int nwg)
         same = cc.mnk[i][0] == a.g[i].m && cc.mnk[i][1] == a.g[i].n && cc.mnk[i][2] == a.g[i].k;
     if (same) {
         memcpy(a.cut, cc.cut, sizeof(int64_t) * (nwg + 1));
+        memcpy(a.start, cc.start, sizeof(uint64_t) * nwg);
         return;
     }
     std::vector<PlanTile> tiles;
@@ -1111,6 +1135,8 @@ void plan_cuts(LaunchArgs &a, int nwg)
             lo = mid;
     }
     greedy_cuts(tiles, nwg, a.total_cost, hi, a.cut);
+    for (int w = 0; w < nwg; ++w)
+        a.start[w] = pack_start(locate(a, a.cut[w]), a.ng);
     cc.nwg = nwg;
     cc.ng = a.ng;
     for (int i = 0; i < a.ng; ++i) {
@@ -1119,6 +1145,7 @@ void plan_cuts(LaunchArgs &a, int nwg)
         cc.mnk[i][2] = a.g[i].k;
     }
     memcpy(cc.cut, a.cut, sizeof(int64_t) * (nwg + 1));
+    memcpy(cc.start, a.start, sizeof(uint64_t) * nwg);
 }
 
 // Library-owned workspace for one stream: partial-sum slots and flags.
@@ -1226,7 +1253,7 @@ extern "C" int nvfp4_plan(const nvfp4_group_t *groups, int ng, int num_workgroup
         for (int w = 0; w < nwg; ++w) {
             const int64_t lo = args.cut[w];
             const int64_t hi = args.cut[w + 1];
-            TilePos p = locate(args, lo);
+            TilePos p = unpack_start(args, args.start[w]);
             while (p.g < args.ng) {
                 const GroupArgs &G = args.g[p.g];
                 int pb, pe;
