@@ -192,3 +192,36 @@ def test_plan_cache_keys_on_sizes():
     near = nv.plan([G(*s) for s in c], 256)
     assert near != first
     assert nv.plan([G(*s) for s in c], 256) == near
+
+@pytest.mark.parametrize("seed", range(24))
+def test_plan_random_shapes(seed):
+    """Random launches: every output element is written once, each tile's k
+    range is covered once in order, a split tile has exactly one finalizer
+    (its first part), and no workgroup runs a producer part after a
+    finalizer part (so no finalizer can wait on a waiting workgroup)."""
+    rng = np.random.default_rng(1000 + seed)
+    ng = int(rng.integers(1, 13))
+    shapes = [(int(rng.integers(0, 400)), int(rng.integers(0, 3000)), 64 * int(rng.integers(0, 120)))
+              for _ in range(ng)]
+    for num_wg in (1, 7, 64, 256):
+        segs = nv.plan([G(*s) for s in shapes], num_wg)
+        cover = [np.zeros((m, n), np.int8) for (m, n, k) in shapes]
+        by_tile, by_wg = {}, {}
+        for seg in segs:
+            wg, g, m0, rows, n0, kb, ke, role = seg
+            assert 0 <= wg < num_wg and 0 < rows and kb < ke
+            by_tile.setdefault(_tile_key(seg), []).append(seg)
+            by_wg.setdefault(wg, []).append(role)
+            if role in (0, 2):
+                cover[g][m0:m0 + rows, n0:n0 + 256] += 1
+        for (m, n, k), cv in zip(shapes, cover):
+            assert (cv == 1).all()
+        for key, parts in by_tile.items():
+            parts.sort(key=lambda q: q[5])
+            k = shapes[key[0]][2]
+            assert parts[0][5] == 0 and parts[-1][6] == 256 * max(1, -(-k // 256))
+            assert all(a[6] == b[5] for a, b in zip(parts, parts[1:]))
+            assert [q[7] for q in parts] == ([0] if len(parts) == 1 else [2] + [1] * (len(parts) - 1))
+        for roles in by_wg.values():
+            if 2 in roles:
+                assert 1 not in roles[roles.index(2):]

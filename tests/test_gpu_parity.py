@@ -63,6 +63,17 @@ def test_small_ragged_shapes(seed):
     check_full(workloads.generate(w), "ragged seed %d" % seed)
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_random_shapes_full(seed):
+    """Random groups (some empty, ragged M and N, K from 64 to 3072) through
+    the whole schedule, compared element by element."""
+    rng = np.random.default_rng(500 + seed)
+    shapes = [(int(rng.integers(0, 260)), int(rng.integers(0, 700)), 64 * int(rng.integers(1, 49)))
+              for _ in range(int(rng.integers(2, 9)))]
+    w = workloads.make_workload(shapes, e_range=(-6, 3), seed=500 + seed)
+    check_full(workloads.generate(w), "random seed %d" % seed)
+
+
 def test_config0_full():
     check_full(workloads.generate(workloads.CONFIGS[0]), workloads.CONFIGS[0].name)
 
