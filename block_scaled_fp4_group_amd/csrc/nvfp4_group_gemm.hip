@@ -17,12 +17,16 @@
 //  * Workgroup = 8 waves, output tile = up to 128 rows x 256 columns of one
 //    group.  Per 128-k stage the waves decode the tile's A rows once into LDS
 //    (fragment-major, so every MFMA operand read is one conflict-free
-//    ds_read_b128), while each wave streams and decodes its own 32 columns of
-//    B straight from HBM into registers.  LDS stages are double-buffered and
-//    raw HBM loads are issued two stages ahead.  The waves hand the shared
-//    A operands over through two LDS counters instead of a barrier per
-//    stage, so they drift apart and one wave's decode overlaps another's
-//    MFMAs.
+//    ds_read_b128), while each wave decodes its own 32 columns of B into
+//    registers.  Raw codes and scales arrive by direct HBM-to-LDS loads,
+//    issued two stages ahead into a wave-private ring; the decoded A
+//    operands are double-buffered.  The waves hand the shared A operands
+//    over through two LDS counters instead of a barrier per stage, so they
+//    drift apart and one wave's decode overlaps another's MFMAs.
+//  * One workgroup per CU, each with one contiguous range of the launch's
+//    (tile, 256-k pair) units ("stream-K"); the host balances the ranges
+//    with a clock model of the kernel, and a tile split between workgroups
+//    is summed by the one holding its first pair.
 //  * Inside a 128-k stage lane (r, q) of a wave holds k = 32q + 8s + [0, 8)
 //    at MFMA step s; A and B use the same permutation of k, which leaves the
 //    sum unchanged and lets every lane read 16 contiguous bytes per row.
