@@ -42,6 +42,8 @@ def parse():
     p.add_argument("--warm-cache", action="store_true", help="reuse one replica (numbers labelled warm)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--all-configs", action="store_true", help="also report every workload on stderr")
+    p.add_argument("--oracle-timing", action="store_true",
+                   help="time the oracle on every workload with 1 thread and with all threads, then exit")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                    help="run one plain device-to-device copy of BYTES first (counter calibration)")
     return p.parse_args()
@@ -171,8 +173,27 @@ def cpu_baseline(w, groups, budget_s=20.0):
             % (used, len(groups), w.name, fl / 1e9, dt)}
 
 
+def oracle_timing():
+    """The oracle as it stands on every workload, whole, once with one
+    thread and once with all host threads: one JSON line each."""
+    import oracle
+    for w in workloads.CONFIGS:
+        groups = workloads.generate(w)
+        flops = workloads.config_flops(w.shapes)
+        for nt in (1, oracle.max_threads()):
+            t0 = time.perf_counter()
+            for g in groups:
+                oracle.gemm_group(g.a, g.sfa, g.b, g.sfb, g.m, g.n, g.k, nt)
+            dt = time.perf_counter() - t0
+            print(json.dumps({"workload": w.name, "threads": nt, "seconds": round(dt, 3),
+                              "tflops": round(flops / dt / 1e12, 6), "kind": "oracle"}), flush=True)
+
+
 def main():
     args = parse()
+    if args.oracle_timing:
+        oracle_timing()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (the grouped GEMM shards by group or "
               "by N with no exchange; multi-GPU runs are not part of it). Use --gpus 1.",
