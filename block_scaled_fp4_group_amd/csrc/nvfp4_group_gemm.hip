@@ -113,8 +113,11 @@ struct LaunchArgs {
     int32_t num_wg;      // workgroups of the launch
     int64_t total_cost;
     float *partials;     // num_wg slots of kPartialSlot bytes
-    uint32_t *flags;     // num_wg flags: slot holds this launch's partial when == epoch
-    uint32_t epoch;
+    uint32_t *flags;     // num_wg flags: slot holds this launch's partial when == its epoch
+    // [0]: epoch of the last finished launch on this workspace, [1]:
+    // workgroups of this launch that have finished (device-resident, so a
+    // launch replayed from a captured graph still gets a fresh epoch)
+    uint32_t *control;
     int32_t spin_limit;  // flag polls before a missing part is recomputed instead
     // Workgroup w's range is the cost interval (cut[w], cut[w + 1]]: the
     // pairs whose end cost lies in it belong to w (cut[0] = 0, cut[num_wg] =
@@ -744,7 +747,7 @@ __device__ __forceinline__ int partial_base(int slot, int wave)
 
 // Producer side: publish the partial sums of this workgroup's first segment.
 template <int NRB>
-__device__ __forceinline__ void publish_partial(const LaunchArgs &args, int slot, int wave,
+__device__ __forceinline__ void publish_partial(const LaunchArgs &args, uint32_t epoch, int slot, int wave,
                                                 const f32x4 (&outer)[NRB][2])
 {
     const int lane = lane_id();
@@ -758,11 +761,11 @@ __device__ __forceinline__ void publish_partial(const LaunchArgs &args, int slot
     wait_vmcnt<0>();               // every store of this wave has reached the coherence point
     __syncthreads();
     if (threadIdx.x == 0)
-        __hip_atomic_store(&args.flags[slot], args.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&args.flags[slot], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Finalizer side: wait (bounded) for producer `slot`; true if its sums arrived.
-__device__ __forceinline__ bool await_partial(const LaunchArgs &args, int slot)
+__device__ __forceinline__ bool await_partial(const LaunchArgs &args, uint32_t epoch, int slot)
 {
     __shared__ int ready;
     if (threadIdx.x == 0) {
@@ -771,7 +774,7 @@ __device__ __forceinline__ bool await_partial(const LaunchArgs &args, int slot)
         // resident) makes the caller compute that part itself instead of
         // waiting forever
         for (int it = 0; it < args.spin_limit; ++it) {
-            if (__hip_atomic_load(&args.flags[slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == args.epoch) {
+            if (__hip_atomic_load(&args.flags[slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch) {
                 ok = 1;
                 break;
             }
@@ -810,7 +813,7 @@ __device__ __forceinline__ void add_partial(const LaunchArgs &args, int slot, in
 // One tile's share of this workgroup: pairs [pb, pe).  `w` is the logical
 // workgroup index, [lo, hi) its cost range.
 template <int NRB, int W>
-__device__ __forceinline__ void run_tile(const LaunchArgs &args, const TilePos &p, int pb, int pe, int w,
+__device__ __forceinline__ void run_tile(const LaunchArgs &args, uint32_t epoch, const TilePos &p, int pb, int pe, int w,
                                          int wave, uint8_t *smem)
 {
     const GroupArgs &G = args.g[p.g];
@@ -828,7 +831,7 @@ __device__ __forceinline__ void run_tile(const LaunchArgs &args, const TilePos &
     for (;;) {
         segment<NRB, W>(G, m0, n0, wave, smem, sb, se, outer);
         if (pb > 0) {              // a later part of a split tile
-            publish_partial<NRB>(args, w, wave, outer);
+            publish_partial<NRB>(args, epoch, w, wave, outer);
             return;
         }
         // finalizer: add the other parts of the tile in k order
@@ -843,7 +846,7 @@ __device__ __forceinline__ void run_tile(const LaunchArgs &args, const TilePos &
             pairs_in(p, G.npairs, lo, hi, qb, qe);
             if (qb >= qe)
                 continue;
-            if (await_partial(args, w2)) {
+            if (await_partial(args, epoch, w2)) {
                 add_partial<NRB>(args, w2, wave, outer);
             } else {
                 sb = qb;
@@ -868,6 +871,11 @@ __global__ __launch_bounds__(64 * W, 1) void nvfp4_group_gemm_kernel(const Launc
     const int b = blockIdx.x, nwg = args.num_wg;
     const int w = (nwg % 8 == 0) ? (b % 8) * (nwg / 8) + b / 8 : b;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // this launch's epoch: one past the last finished launch's (0 marks an
+    // unwritten flag); no workgroup changes it before all have started
+    const uint32_t last = (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)__hip_atomic_load(&args.control[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    const uint32_t epoch = last + 1u == 0u ? 1u : last + 1u;
     const int64_t lo = args.cut[w];
     const int64_t hi = args.cut[w + 1];
 
@@ -879,18 +887,29 @@ __global__ __launch_bounds__(64 * W, 1) void nvfp4_group_gemm_kernel(const Launc
         if (pb >= pe)
             break;
         switch (p.nrb) {
-        case 1: run_tile<1, W>(args, p, pb, pe, w, wave, smem); break;
-        case 2: run_tile<2, W>(args, p, pb, pe, w, wave, smem); break;
-        case 3: run_tile<3, W>(args, p, pb, pe, w, wave, smem); break;
-        case 4: run_tile<4, W>(args, p, pb, pe, w, wave, smem); break;
-        case 5: run_tile<5, W>(args, p, pb, pe, w, wave, smem); break;
-        case 6: run_tile<6, W>(args, p, pb, pe, w, wave, smem); break;
-        case 7: run_tile<7, W>(args, p, pb, pe, w, wave, smem); break;
-        default: run_tile<8, W>(args, p, pb, pe, w, wave, smem); break;
+        case 1: run_tile<1, W>(args, epoch, p, pb, pe, w, wave, smem); break;
+        case 2: run_tile<2, W>(args, epoch, p, pb, pe, w, wave, smem); break;
+        case 3: run_tile<3, W>(args, epoch, p, pb, pe, w, wave, smem); break;
+        case 4: run_tile<4, W>(args, epoch, p, pb, pe, w, wave, smem); break;
+        case 5: run_tile<5, W>(args, epoch, p, pb, pe, w, wave, smem); break;
+        case 6: run_tile<6, W>(args, epoch, p, pb, pe, w, wave, smem); break;
+        case 7: run_tile<7, W>(args, epoch, p, pb, pe, w, wave, smem); break;
+        default: run_tile<8, W>(args, epoch, p, pb, pe, w, wave, smem); break;
         }
         if (pe < npairs)
             break;                 // the range ends inside this tile
         p = next_tile(args.g, args.ng, args.total_cost, p);
+    }
+    // The last workgroup to finish resets the count and records the epoch
+    // for the next launch on this workspace (ordered after this one by the
+    // stream).
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t done = __hip_atomic_fetch_add(&args.control[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (done == (uint32_t)nwg - 1u) {
+            __hip_atomic_store(&args.control[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&args.control[0], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
 }
 
@@ -1152,12 +1171,13 @@ void plan_cuts(LaunchArgs &a, int nwg)
     memcpy(cc.start, a.start, sizeof(uint64_t) * nwg);
 }
 
-// Library-owned workspace for one stream: partial-sum slots and flags.
+// Library-owned workspace for one stream: partial-sum slots, their flags,
+// and two control words after the flags (the epoch of the last finished
+// launch and a count of finished workgroups).
 struct Workspace {
     float *partials = nullptr;
     uint32_t *flags = nullptr;
     int slots = 0;
-    uint32_t epoch = 0;
 };
 
 std::mutex g_ws_mutex;
@@ -1181,13 +1201,12 @@ int workspace_for(hipStream_t st, int device, int slots, Workspace *&out)
         }
         hipError_t e = hipMalloc(reinterpret_cast<void **>(&ws.partials), (size_t)slots * kPartialSlot);
         if (e == hipSuccess)
-            e = hipMalloc(reinterpret_cast<void **>(&ws.flags), (size_t)slots * sizeof(uint32_t));
+            e = hipMalloc(reinterpret_cast<void **>(&ws.flags), ((size_t)slots + 2) * sizeof(uint32_t));
         if (e == hipSuccess)
-            e = hipMemsetAsync(ws.flags, 0, (size_t)slots * sizeof(uint32_t), st);
+            e = hipMemsetAsync(ws.flags, 0, ((size_t)slots + 2) * sizeof(uint32_t), st);
         if (e != hipSuccess)
             return fail(NVFP4_EHIP, "workspace allocation failed: %s", hipGetErrorString(e));
         ws.slots = slots;
-        ws.epoch = 0;
     }
     out = &ws;
     return NVFP4_OK;
@@ -1316,9 +1335,7 @@ extern "C" int nvfp4_group_gemm(const nvfp4_group_t *groups, int ng, void *strea
         plan_cuts(args, nwg);
         args.partials = ws->partials;
         args.flags = ws->flags;
-        if (++ws->epoch == 0)
-            ++ws->epoch;       // 0 marks an unwritten flag
-        args.epoch = ws->epoch;
+        args.control = ws->flags + ws->slots;
         args.spin_limit = spin_limit();
         hipLaunchKernelGGL((nvfp4_group_gemm_kernel<kWaves>), dim3((unsigned)nwg), dim3(kThreads), 0, st, args);
         const hipError_t e = hipGetLastError();

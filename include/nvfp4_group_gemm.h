@@ -84,6 +84,13 @@ typedef struct nvfp4_group {
  * does not arrive in time itself.  The environment variable
  * NVFP4_SPIN_LIMIT (read at each call) sets the number of polls of that
  * wait; 0 makes every such part be recomputed (used to test that path).
+ * Graphs: the call keeps no per-call host state (the epoch that tells a
+ * split tile's partial sums of this launch from older ones lives in the
+ * workspace and is advanced by the kernel), so it may be captured in a HIP
+ * graph and replayed, once its stream's workspace exists (a first call on
+ * that stream outside capture creates it; capture itself allocates
+ * nothing after that).  Replays of one captured call are ordered by the
+ * stream like calls.
  * Host cost: each launch of up to 32 groups uses at most min(compute units,
  * 256) workgroups, whose work ranges the host balances with a timing model
  * of the kernel (tens of microseconds); the last result is reused, per host
