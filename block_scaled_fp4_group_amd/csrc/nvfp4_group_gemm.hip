@@ -393,11 +393,19 @@ constexpr int kSyncSpinLimit = 1 << 14;
 // Both are single asm statements so that the hot loop stays one basic
 // block for the compiler; the LDS operations they add only make the
 // compiler's own (in-order) LDS waits more conservative.
-__device__ __forceinline__ void half_wait(uint32_t count_addr, int target)
+// `pre` is the counter as read some MFMA steps earlier by a plain LDS load:
+// the counter only grows, so if that value already meets the target the
+// wait ends without a new read (whose lgkmcnt(0) would drain every LDS
+// operation in flight), and the compiler's wait for `pre` covers only the
+// LDS operations issued before it.
+__device__ __forceinline__ void half_wait(uint32_t count_addr, int target, int pre)
 {
     int v;
     int seen, left = kSyncSpinLimit;
-    asm volatile("1:\n\t"
+    asm volatile("v_readfirstlane_b32 %1, %5\n\t"
+                 "s_cmp_ge_i32 %1, %4\n\t"
+                 "s_cbranch_scc1 2f\n"
+                 "1:\n\t"
                  "ds_read_b32 %0, %3\n\t"
                  "s_waitcnt lgkmcnt(0)\n\t"
                  "v_readfirstlane_b32 %1, %0\n\t"
@@ -409,8 +417,15 @@ __device__ __forceinline__ void half_wait(uint32_t count_addr, int target)
                  "s_cbranch_scc1 1b\n"
                  "2:"
                  : "=&v"(v), "=&s"(seen), "+s"(left)
-                 : "v"(count_addr), "s"(target)
+                 : "v"(count_addr), "s"(target), "v"(pre)
                  : "memory", "scc");
+}
+// Early read of a counter for half_wait (a volatile LDS load, so it stays
+// where it is issued relative to the other LDS operations).
+typedef __attribute__((address_space(3))) const volatile int lds_cvint;
+__device__ __forceinline__ int count_read(uint32_t count_addr)
+{
+    return *reinterpret_cast<lds_cvint *>((uintptr_t)count_addr);
 }
 __device__ __forceinline__ void half_done(uint32_t count_addr, uint32_t one)
 {
@@ -561,6 +576,7 @@ __device__ __forceinline__ void segment(const GroupArgs &G, int m0, int n0, int 
     if (threadIdx.x < 2)
         sync[threadIdx.x] = 0;     // no wave counts again before this barrier
     __syncthreads();
+    int pre0 = 0;       // early read of counter 0 for the next stage (the first stage needs none)
 
     // Stage c: fetch the codes of stage c + 3 into the ring slot stage c used
     // (and, on odd stages, the scale window of stages c + 3 and c + 4 into the
@@ -592,15 +608,16 @@ __device__ __forceinline__ void segment(const GroupArgs &G, int m0, int n0, int 
         }
         const u32x4 ac_next = a_codes(nslot);
         const int ready = __builtin_amdgcn_readfirstlane(kWaves * (c - c_begin));
-        half_wait(sync_addr, ready);
+        half_wait(sync_addr, ready, pre0);
 #pragma unroll
         for (int i = 0; i < NRB; ++i)
             af[i] = aop(kBuf, i, 0);
+        int pre1 = 0;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             __builtin_amdgcn_sched_barrier(0);
             if (s == 1)
-                half_wait(sync_addr + 4u, ready);   // step 2's fragments are read during step 1
+                half_wait(sync_addr + 4u, ready, pre1);   // step 2's fragments are read during step 1
 #pragma unroll
             for (int i = 0; i < NRB; ++i) {
 #pragma unroll
@@ -609,6 +626,15 @@ __device__ __forceinline__ void segment(const GroupArgs &G, int m0, int n0, int 
                         af[i], bf[cb][s], (kFirst && s == 0) ? f32x4{0.f, 0.f, 0.f, 0.f} : inner[i][cb], 0, 0, 0);
                 if (s < 3)
                     af[i] = aop(kBuf, i, s + 1);
+                // early counter reads, half a step (second half of this
+                // stage's A) or one and a half steps (first half of the next
+                // stage's A) before they are checked
+                if (i == (NRB - 1) / 2) {
+                    if (s == 0)
+                        pre1 = count_read(sync_addr + 4u);
+                    else if (s == 3)
+                        pre0 = count_read(sync_addr);
+                }
             }
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb) {
@@ -1049,13 +1075,24 @@ int grid_for(const LaunchArgs &args, int units)
 //    part (one other part if the next workgroup can take the rest of the
 //    tile, else two);
 //  * a middle part (a workgroup whose whole range lies inside the tile): its
-//    publish must leave the finalizer time for two sums and the store.
-constexpr double kClkStart = 7000;
-constexpr double kClkFillFirst = 14200;
+//    publish must leave the finalizer time for two sums and the store;
+//  * the last part of a split tile: its publish must leave the finalizer
+//    time for one sum and the store (the finalizer ends after the last part
+//    arrives, so a last part that ends at the makespan would set the
+//    makespan one sum and a store later).
+// Start-up, fills, store and publish are a least-squares fit of per-
+// workgroup timestamps (segment entry, loop start and end, kernel entry and
+// exit) over seven workloads; start-up and the first fill include the
+// workgroup's end-of-kernel work.  The pair costs, measured per tile height
+// on the balanced schedule, sit 6-14% above the bare loop's cost: they also
+// carry what a segment of short tiles pays beyond its loop, and a table
+// fitted to the loop alone balanced the ragged workloads worse.
+constexpr double kClkStart = 3500;
+constexpr double kClkFillFirst = 5850;
 constexpr double kClkFillNext = 9400;
 constexpr double kClkPair[kRowBlocks + 1] = {0, 4212, 4634, 4648, 4880, 5305, 5622, 6141, 6988};
-constexpr double kClkPublish = 3300;
-constexpr double kClkStore = 5000;
+constexpr double kClkPublish = 7900;
+constexpr double kClkStore = 7200;
 constexpr double kClkAdd = 4000;
 
 // One tile of the launch for the partition: where it starts in cost order,
@@ -1080,7 +1117,9 @@ bool greedy_cuts(const std::vector<PlanTile> &tiles, int nwg, int64_t total, dou
             const double base = cur + (fresh ? kClkFillFirst : kClkFillNext);
             const int rest = npairs - j;
             const double epi_full = j == 0 ? kClkStore : kClkPublish;
-            if (base + rest * pc + epi_full <= tmax) {   // the rest of the tile fits
+            // a last part of a split tile leaves the finalizer its sum and store
+            const double tail = j == 0 ? 0.0 : kClkAdd + kClkStore;
+            if (base + rest * pc + epi_full + tail <= tmax) {   // the rest of the tile fits
                 cur = base + rest * pc + epi_full;
                 fresh = false;
                 break;
@@ -1091,7 +1130,7 @@ bool greedy_cuts(const std::vector<PlanTile> &tiles, int nwg, int64_t total, dou
                 return fit < 0 ? 0 : (fit > rest - 1 ? rest - 1 : (int)fit);
             };
             auto next_takes_rest = [&](int r) {
-                return kClkStart + kClkFillFirst + r * pc + kClkPublish <= tmax;
+                return kClkStart + kClkFillFirst + r * pc + kClkPublish + kClkAdd + kClkStore <= tmax;
             };
             int k;
             if (j == 0) {

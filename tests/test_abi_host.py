@@ -143,10 +143,10 @@ PAIR_CLK = [0, 4212, 4634, 4648, 4880, 5305, 5622, 6141, 6988]
 
 def test_plan_balances_work():
     """The partition balances the workgroups' modelled times.  The model,
-    in clocks: start-up 7000; a fill of 14200 for a workgroup's first
+    in clocks: start-up 3500; a fill of 5850 for a workgroup's first
     segment and 9400 for each later one; per pair 4212, 4634, 4648, 4880,
-    5305, 5622, 6141, 6988 for 1..8 row blocks of 16; after a segment 3300
-    to publish a part of a split tile, or 5000 to store a tile plus 4000
+    5305, 5622, 6141, 6988 for 1..8 row blocks of 16; after a segment 7900
+    to publish a part of a split tile, or 7200 to store a tile plus 4000
     per other part to sum.  At least 95% of the
     compute units get work (the greedy fill may leave a few idle when whole
     tiles pack better), and the slowest is within 12% of the mean of those
@@ -163,13 +163,43 @@ def test_plan_balances_work():
             parts[_tile_key(seg)] += 1
         t = np.zeros(256)
         for wg, own in by_wg.items():
-            x = 7000.0
+            x = 3500.0
             for i, (_, g, m0, rows, n0, kb, ke, role) in enumerate(own):
-                x += (14200 if i == 0 else 9400) + (ke - kb) // 256 * PAIR_CLK[-(-rows // 16)]
-                x += 3300 if role == 1 else 5000 + 4000 * (parts[_tile_key(own[i])] - 1)
+                x += (5850 if i == 0 else 9400) + (ke - kb) // 256 * PAIR_CLK[-(-rows // 16)]
+                x += 7900 if role == 1 else 7200 + 4000 * (parts[_tile_key(own[i])] - 1)
             t[wg] = x
         assert (t > 0).mean() >= 0.95
         assert t.max() <= 1.12 * t[t > 0].mean()
+
+
+def test_plan_leaves_finalizers_their_tail():
+    """Under the same model, the last part of every split tile is published
+    early enough that the finalizer's sum of it (4000) and its store (7200)
+    still end within the makespan: a last part that ran up to the makespan
+    would make its finalizer the slowest workgroup."""
+    from collections import defaultdict
+    for shapes in ([(m, 4096, 7168) for m in (80, 176, 128, 72, 64, 248, 96, 160)],
+                   [(384, 3072, 4096), (512, 3072, 4096)],
+                   [(1, 8192, 7168), (17, 8192, 7168), (129, 4096, 2048), (255, 2048, 4096),
+                    (512, 1024, 256), (33, 6144, 1536), (300, 3072, 7168), (8, 512, 512)]):
+        segs = nv.plan([G(*s) for s in shapes], 256)
+        by_wg = defaultdict(list)
+        parts = defaultdict(int)
+        for seg in segs:
+            by_wg[seg[0]].append(seg)
+            parts[_tile_key(seg)] += 1
+        end, last_publish = {}, []
+        for wg, own in by_wg.items():
+            x = 3500.0
+            for i, (_, g, m0, rows, n0, kb, ke, role) in enumerate(own):
+                x += (5850 if i == 0 else 9400) + (ke - kb) // 256 * PAIR_CLK[-(-rows // 16)]
+                x += 7900 if role == 1 else 7200 + 4000 * (parts[_tile_key(own[i])] - 1)
+                if role == 1 and ke == shapes[g][2]:
+                    last_publish.append(x)
+            end[wg] = x
+        makespan = max(end.values())
+        assert last_publish, "no split tiles: the case tests nothing"
+        assert max(last_publish) + 4000 + 7200 <= makespan * 1.001
 
 
 def test_plan_rejects_invalid():
