@@ -583,7 +583,8 @@ __device__ __forceinline__ void segment(const GroupArgs &G, int m0, int n0, int 
     // window buffer the stages before c used); wait for stage c + 1; per MFMA step s: 2 * NRB MFMAs on the A fragments of step s
     // (read from LDS; a row block's fragment for step s + 1 is read right
     // after its last use), then step s of B (stage c + 1) is decoded into the
-    // freed bf slot and step s of A (stage c + 1) into the other LDS buffer.
+    // freed bf slot and step s of A (stage c + 1) into the other LDS buffer
+    // (step 0 of A right after the top-of-stage reads, which it covers).
     // Each half of stage c's A is read only after every wave has written it
     // (half_wait), and each written half of stage c + 1 is counted
     // (half_done).  The last stage decodes unused data instead of branching.
@@ -612,6 +613,8 @@ __device__ __forceinline__ void segment(const GroupArgs &G, int m0, int n0, int 
 #pragma unroll
         for (int i = 0; i < NRB; ++i)
             af[i] = aop(kBuf, i, 0);
+        // step 0 of the next stage's A while this stage's step-0 reads land
+        decode_a_into(ac_next, sa_next, kNext, 0);
         int pre1 = 0;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -641,7 +644,8 @@ __device__ __forceinline__ void segment(const GroupArgs &G, int m0, int n0, int 
                 bf[cb][s] = operand(bc_next[cb][s], sb_next[cb], s);
                 asm volatile("" : "+v"(bf[cb][s]));   // keep the decode inside step s
             }
-            decode_a_into(ac_next, sa_next, kNext, s);
+            if (s > 0)
+                decode_a_into(ac_next, sa_next, kNext, s);
             if (s & 1)
                 half_done(sync_addr + 4u * (s >> 1), one);
         }
