@@ -1090,14 +1090,17 @@ int grid_for(const LaunchArgs &args, int units)
 // workgroup's end-of-kernel work.  The pair costs, measured per tile height
 // on the balanced schedule, sit 6-14% above the bare loop's cost: they also
 // carry what a segment of short tiles pays beyond its loop, and a table
-// fitted to the loop alone balanced the ragged workloads worse.
+// fitted to the loop alone balanced the ragged workloads worse.  The cost of
+// a finalizer's sum of one part (6000) is the value interleaved timing
+// preferred over 4000 and 8000: finalizers end 15-19k clk after their
+// tile's last part, more than one sum and a store at the fitted costs.
 constexpr double kClkStart = 3500;
 constexpr double kClkFillFirst = 5850;
 constexpr double kClkFillNext = 9400;
 constexpr double kClkPair[kRowBlocks + 1] = {0, 4212, 4634, 4648, 4880, 5305, 5622, 6141, 6988};
 constexpr double kClkPublish = 7900;
 constexpr double kClkStore = 7200;
-constexpr double kClkAdd = 4000;
+constexpr double kClkAdd = 6000;
 
 // One tile of the launch for the partition: where it starts in cost order,
 // its pair cost there, and its pairs' modelled clocks.

@@ -146,7 +146,7 @@ def test_plan_balances_work():
     in clocks: start-up 3500; a fill of 5850 for a workgroup's first
     segment and 9400 for each later one; per pair 4212, 4634, 4648, 4880,
     5305, 5622, 6141, 6988 for 1..8 row blocks of 16; after a segment 7900
-    to publish a part of a split tile, or 7200 to store a tile plus 4000
+    to publish a part of a split tile, or 7200 to store a tile plus 6000
     per other part to sum.  At least 95% of the
     compute units get work (the greedy fill may leave a few idle when whole
     tiles pack better), and the slowest is within 12% of the mean of those
@@ -166,7 +166,7 @@ def test_plan_balances_work():
             x = 3500.0
             for i, (_, g, m0, rows, n0, kb, ke, role) in enumerate(own):
                 x += (5850 if i == 0 else 9400) + (ke - kb) // 256 * PAIR_CLK[-(-rows // 16)]
-                x += 7900 if role == 1 else 7200 + 4000 * (parts[_tile_key(own[i])] - 1)
+                x += 7900 if role == 1 else 7200 + 6000 * (parts[_tile_key(own[i])] - 1)
             t[wg] = x
         assert (t > 0).mean() >= 0.95
         assert t.max() <= 1.12 * t[t > 0].mean()
@@ -174,7 +174,7 @@ def test_plan_balances_work():
 
 def test_plan_leaves_finalizers_their_tail():
     """Under the same model, the last part of every split tile is published
-    early enough that the finalizer's sum of it (4000) and its store (7200)
+    early enough that the finalizer's sum of it (6000) and its store (7200)
     still end within the makespan: a last part that ran up to the makespan
     would make its finalizer the slowest workgroup."""
     from collections import defaultdict
@@ -193,13 +193,13 @@ def test_plan_leaves_finalizers_their_tail():
             x = 3500.0
             for i, (_, g, m0, rows, n0, kb, ke, role) in enumerate(own):
                 x += (5850 if i == 0 else 9400) + (ke - kb) // 256 * PAIR_CLK[-(-rows // 16)]
-                x += 7900 if role == 1 else 7200 + 4000 * (parts[_tile_key(own[i])] - 1)
+                x += 7900 if role == 1 else 7200 + 6000 * (parts[_tile_key(own[i])] - 1)
                 if role == 1 and ke == shapes[g][2]:
                     last_publish.append(x)
             end[wg] = x
         makespan = max(end.values())
         assert last_publish, "no split tiles: the case tests nothing"
-        assert max(last_publish) + 4000 + 7200 <= makespan * 1.001
+        assert max(last_publish) + 6000 + 7200 <= makespan * 1.001
 
 
 def test_plan_rejects_invalid():
