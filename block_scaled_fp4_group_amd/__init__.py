@@ -13,7 +13,7 @@ from typing import Iterable, List, Sequence, Tuple
 
 __all__ = ["NVFP4_OK", "NVFP4_EINVAL", "NVFP4_EUNSUPPORTED", "NVFP4_EHIP", "Nvfp4Error",
            "Nvfp4Group", "lib", "library_path", "group_gemm", "group_gemm_raw", "validate",
-           "plan", "tile_rows", "tile_cols", "make_group"]
+           "plan", "release_workspace", "tile_rows", "tile_cols", "make_group"]
 
 NVFP4_OK, NVFP4_EINVAL, NVFP4_EUNSUPPORTED, NVFP4_EHIP = 0, 1, 2, 3
 
@@ -50,6 +50,8 @@ def lib():
         L.nvfp4_validate.argtypes = [gp, ctypes.c_int]
         L.nvfp4_plan.restype = ctypes.c_int
         L.nvfp4_plan.argtypes = [gp, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int32), ctypes.c_int]
+        L.nvfp4_release_workspace.restype = ctypes.c_int
+        L.nvfp4_release_workspace.argtypes = [ctypes.c_void_p]
         L.nvfp4_tile_rows.restype = ctypes.c_int
         L.nvfp4_tile_cols.restype = ctypes.c_int
         L.nvfp4_last_error.restype = ctypes.c_char_p
@@ -97,6 +99,14 @@ def plan(groups: Sequence[Nvfp4Group], num_workgroups: int = 256) -> List[Tuple[
     n2 = lib().nvfp4_plan(arr, len(groups), num_workgroups, buf, n)
     assert n2 == n
     return [tuple(buf[8 * i:8 * i + 8]) for i in range(n)]
+
+
+def release_workspace(stream: int = 0) -> None:
+    """Free the library's workspace of the current device and a raw
+    hipStream_t (after the work queued on it)."""
+    rc = lib().nvfp4_release_workspace(ctypes.c_void_p(stream or None))
+    if rc != NVFP4_OK:
+        raise Nvfp4Error(rc, _last_error())
 
 
 def tile_rows() -> int:

@@ -16,9 +16,6 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # packed fp32 VALU ops are kept out of the generated code on purpose
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # MFMA accumulators in arch VGPRs with dst == srcC: the AGPR form makes the
-    # register allocator copy every loop-carried accumulator each iteration
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -69,14 +69,17 @@ typedef struct nvfp4_group {
  *                       k % 16 != 0; c == NULL in a group with m, n > 0; a,
  *                       b, sfa or sfb == NULL in such a group with k > 0;
  *                       reserved != 0.
- *   NVFP4_EUNSUPPORTED  k % 64 != 0 (the kernels read scales four at a time);
- *                       a pointer that breaks the alignment stated above.
+ *   NVFP4_EUNSUPPORTED  k % 64 != 0 (the kernel moves k in stages of 64); a
+ *                       pointer that breaks the alignment stated above; m,
+ *                       n times k/2 reaching 2 GiB; the stream is being
+ *                       captured into a graph and has no workspace yet.
  *   NVFP4_EHIP          a workspace allocation or the launch failed (message
  *                       via nvfp4_last_error).
- * Workspace: the first call on a (device, stream) pair allocates a small
- * device workspace for that pair (partial sums of split tiles and their
- * flags, about 128 KiB per compute unit) and keeps it for the life of the
- * process; later calls on that pair allocate nothing.  Calls on one stream
+ * Workspace: the first call on a (device, stream) pair allocates a device
+ * workspace for that pair (partial sums of split tiles and their flags, 128
+ * KiB per compute unit, at most 256 units) and keeps it until
+ * nvfp4_release_workspace(stream) or the end of the process; later calls on
+ * that pair allocate nothing.  Calls on one stream
  * are ordered by the stream; calls on different streams use different
  * workspaces and may run concurrently.
  * Split tiles: a workgroup that finishes a tile waits (bounded) for the
@@ -88,8 +91,8 @@ typedef struct nvfp4_group {
  * split tile's partial sums of this launch from older ones lives in the
  * workspace and is advanced by the kernel), so it may be captured in a HIP
  * graph and replayed, once its stream's workspace exists (a first call on
- * that stream outside capture creates it; capture itself allocates
- * nothing after that).  Replays of one captured call are ordered by the
+ * that stream outside capture creates it; a call on a capturing stream
+ * without one returns NVFP4_EUNSUPPORTED and records nothing).  Replays of one captured call are ordered by the
  * stream like calls.
  * Host cost: each launch of up to 32 groups uses at most min(compute units,
  * 256) workgroups, whose work ranges the host balances with a timing model
@@ -122,6 +125,13 @@ int nvfp4_validate(const nvfp4_group_t *groups, int ng);
  * the records of each batch follow those of the previous one.
  */
 int nvfp4_plan(const nvfp4_group_t *groups, int ng, int num_workgroups, int32_t *segs, int cap);
+
+/*
+ * Frees the workspace of (current device, stream), after waiting for the
+ * work queued on `stream`.  A later call on that stream creates a new one.
+ * Returns NVFP4_OK (also when there is none) or NVFP4_EHIP.
+ */
+int nvfp4_release_workspace(void *stream);
 
 /* Largest row and column extent of one tile. */
 int nvfp4_tile_rows(void);

@@ -1,5 +1,5 @@
-"""Helpers for the GPU tests: move seeded groups to the device, run the HIP
-library through its binding, and sample outputs for the oracle."""
+"""Helpers for the GPU tests: move seeded groups to the device and run the
+HIP library through its binding."""
 from __future__ import annotations
 
 import sys
@@ -31,17 +31,3 @@ def run_gpu(groups, stream=None) -> List[np.ndarray]:
     nv.group_gemm(args, stream=stream)
     torch.cuda.synchronize()
     return [a[4].cpu().numpy().view(np.uint16) for a in args]
-
-
-def sample_positions(m, n, count, rng, tile_rows=64, tile_cols=64):
-    """Random positions plus every tile's corners and the ragged edges."""
-    rows = list(rng.integers(0, m, count))
-    cols = list(rng.integers(0, n, count))
-    edge_r = sorted({0, m - 1} | {min(m - 1, x) for t in range(0, m, tile_rows) for x in (t, t + tile_rows - 1)})
-    edge_c = sorted({0, n - 1} | {min(n - 1, x) for t in range(0, n, tile_cols) for x in (t, t + tile_cols - 1)})
-    for r in edge_r:
-        for c in edge_c[:: max(1, len(edge_c) // 64)]:
-            rows.append(r); cols.append(c)
-    for c in edge_c:
-        rows.append(edge_r[len(edge_r) // 2]); cols.append(c)
-    return np.array(rows, np.int32), np.array(cols, np.int32)
