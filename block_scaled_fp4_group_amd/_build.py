@@ -16,6 +16,9 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # packed fp32 VALU ops are kept out of the generated code on purpose
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # private arrays stay in registers (or scratch), never in LDS, whose
+    # every byte the kernel lays out itself
+    "-mllvm", "-disable-promote-alloca-to-lds",
 ]
 
 

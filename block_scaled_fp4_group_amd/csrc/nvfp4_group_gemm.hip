@@ -1,4 +1,4 @@
-// nvfp4_group_gemm.hip -- gfx950 (MI355X) kernel and C ABI of the NVFP4
+// nvfp4_group_gemm.hip -- gfx950 (MI355X) kernels and C ABI of the NVFP4
 // grouped GEMM declared in include/nvfp4_group_gemm.h.
 //
 // Operation (pages "nvfp4 group gemm", kernelindex.com submissions 474067,
@@ -9,32 +9,34 @@
 //
 // gfx950 design (not the pages' tcgen05/TMA/TMEM design):
 //  * CDNA4's block-scaled MFMA takes power-of-two (E8M0) scales per 32 k,
-//    while NVFP4 carries E4M3 scales per 16 k, and a decoded product a*s
-//    needs up to 6 significant bits (more than FP8 holds).  Every E2M1 x
-//    E4M3FN product lies in [2^-10, 2688] with at most 6 significant bits, so
-//    it is exact in fp16: operands are decoded exactly to fp16 (hardware
-//    FP4->f16 convert, then one packed f16 multiply by the scale) and fed to
-//    v_mfma_f32_32x32x16_f16 with fp32 accumulation.  The 32x32x16 shape
-//    keeps the matrix core at full rate with one wave per SIMD and lets the
-//    decode VALU issue while it runs.
-//  * Workgroup = 4 waves (one per SIMD), output tile = up to 128 rows x 256
-//    columns of one group.  Wave w owns columns [64 w, 64 w + 64) of the tile
-//    and every row of it, and decodes both its B columns and the tile's A
-//    rows itself, straight into MFMA operand registers, one MFMA step ahead.
-//    Raw codes and scales arrive by direct HBM-to-LDS loads into a ring of
-//    kRing 64-k stages that belongs to the wave alone, so the waves never
-//    wait for each other inside the loop.
+//    while NVFP4 carries E4M3 scales per 16 k.  Every E2M1 x E4M3FN product
+//    has at most 6 significant bits and lies in [2^-10, 2688], so it is exact
+//    in fp16.  Operands are decoded exactly to fp16 (hardware FP4->f16
+//    convert, then one packed f16 multiply by the scale) and fed to
+//    v_mfma_f32_16x16x32_f16 with fp32 accumulation.
+//  * Workgroup = 8 waves, output tile = up to 128 rows x 256 columns of one
+//    group.  Per 128-k stage the waves decode the tile's A rows once into LDS
+//    (fragment-major, so every MFMA operand read is one conflict-free
+//    ds_read_b128), while each wave decodes its own 32 columns of B into
+//    registers.  Raw codes and scales arrive by direct HBM-to-LDS loads,
+//    issued two stages ahead into a wave-private ring; the decoded A
+//    operands are double-buffered.  The waves hand the shared A operands
+//    over through two LDS counters instead of a barrier per stage, so they
+//    drift apart and one wave's decode overlaps another's MFMAs.
 //  * One workgroup per CU, each with one contiguous range of the launch's
-//    (tile, 256-k unit) sequence ("stream-K"); the host balances the ranges
+//    (tile, 256-k pair) units ("stream-K"); the host balances the ranges
 //    with a clock model of the kernel, and a tile split between workgroups
-//    is summed by the one holding its first unit.
-//  * Inside a 64-k stage lane (r, h) of a wave (r = lane % 32, h = lane / 32)
-//    holds k = 32 h + 8 s + [0, 8) of its row (A) or column (B) at MFMA step
-//    s; A and B use the same permutation of k, which leaves the sum unchanged
-//    and lets every lane fetch 16 contiguous code bytes per row and stage.
+//    is summed by the one holding its first pair.
+//  * Inside a 128-k stage lane (r, q) of a wave holds k = 32q + 8s + [0, 8)
+//    at MFMA step s; A and B use the same permutation of k, which leaves the
+//    sum unchanged and lets every lane read 16 contiguous bytes per row.
 //  * Accuracy: the MFMA accumulators restart from zero every 512 k and are
 //    then added into a separate fp32 sum, so rounding happens at the
-//    magnitude of 512-k partial sums instead of the running total.
+//    magnitude of 512-k partial sums instead of the full sum.  An output
+//    whose exact value is small next to the tile's typical partial sums
+//    (heavy cancellation) can still carry more absolute error than the
+//    tolerance allows; each finished tile estimates that error from its own
+//    sums and recomputes the few outputs at risk exactly (fix_small_outputs).
 #include <hip/hip_runtime.h>
 #include <stdarg.h>
 #include <stdint.h>
@@ -43,10 +45,10 @@
 #include <string.h>
 
 #include <map>
+#include <vector>
 #include <mutex>
 #include <type_traits>
 #include <utility>
-#include <vector>
 
 #include "nvfp4_group_gemm.h"
 
@@ -55,41 +57,34 @@ namespace {
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;                       // waves per workgroup (one per SIMD)
+constexpr int kWaves = 8;            // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBlockM = 32;                     // rows of one MFMA block
-constexpr int kRowBlocks = 4;                   // row blocks of a full tile
-constexpr int kTileM = kBlockM * kRowBlocks;    // 128
-constexpr int kWaveCols = 64;                   // columns per wave (two 32-column blocks)
-constexpr int kTileN = kWaveCols * kWaves;      // 256
-constexpr int kStageK = 64;                     // k per pipeline stage (4 MFMA steps of 16)
-constexpr int kUnitK = 256;                     // k per scheduling unit
-constexpr int kStagesPerUnit = kUnitK / kStageK;
-constexpr int kFoldStages = 8;                  // stages summed by MFMA before a fold (512 k)
-constexpr int kRing = 5;                        // stages in a wave's raw-code ring
+constexpr int kTileM = 128;          // max rows of one tile (8 blocks of 16)
+constexpr int kRowBlocks = kTileM / 16;
+constexpr int kTileN = 32 * kWaves;  // columns of one tile (32 per wave)
+constexpr int kStageK = 128;         // k per pipeline stage (4 MFMA steps)
+constexpr int kFoldStages = 4;       // stages summed by MFMA before a fold (512 k)
 constexpr int kMaxGroupsPerLaunch = 32;
-constexpr int kMaxWorkgroups = 256;             // workgroups of one launch (one per CU on MI355X)
+constexpr int kMaxWorkgroups = 256;   // workgroups of one launch (one per CU on MI355X)
 
 // Work decomposition.  A group's output is cut into tiles of up to kTileM
-// rows (the rows spread evenly over the fewest tiles, rounded up to 32) by
-// kTileN columns; K is cut into units of kUnitK.  The (tile, unit) pairs of a
+// rows (the rows spread evenly over the fewest tiles) by kTileN columns; K
+// is cut into stage pairs of 2 * kStageK.  The (tile, stage pair) units of a
 // launch are ordered group by group, column strip by column strip, row tile
-// by row tile, unit by unit, and every workgroup takes one contiguous range
+// by row tile, pair by pair, and every workgroup takes one contiguous range
 // of that order ("stream-K").  The host chooses the ranges (plan_cuts) by
-// balancing a clock model of each workgroup.  A tile whose units fall into
-// several ranges is finished by the workgroup holding its first unit; the
+// balancing a clock model of each workgroup.  A tile whose pairs fall into
+// several ranges is finished by the workgroup holding its first pair; the
 // others leave fp32 partial sums in a workspace.
-// Positions in the order are cost coordinates: a tile is [head][unit 0]
-// [unit 1]..., a unit of a tile with nrb row blocks spans unit_cost(nrb,
-// nunits) coordinates and a head kCostHead, and a unit belongs to the range
-// (lo, hi] that holds its end.  The host places cuts on unit ends, so these
-// weights only fix the coordinates.
-constexpr int kCostRowBlock = 8;
+// Positions in the order are cost coordinates: a tile is [head][pair 0]
+// [pair 1]..., a pair of a tile with nrb row blocks spans pair_cost(nrb,
+// npairs) units and a head kCostHead, and a pair belongs to the range
+// (lo, hi] that holds its end.  The host places cuts on pair ends, so these
+// weights only fix the coordinates (their values were an earlier cost
+// estimate, in units of about 127 clocks).
+constexpr int kCostRowBlock = 4;
 constexpr int kCostFixed = 29;
 constexpr int kCostHead = 60;
 constexpr int kCostSpread = 40;
@@ -102,11 +97,11 @@ struct GroupArgs {
     _Float16 *c;
     int32_t m, n, k;
     int32_t row_tiles;   // tiles along M
-    int32_t tile_rows;   // rows per tile (multiple of 32, <= kTileM)
+    int32_t tile_rows;   // rows per tile (multiple of 16, <= kTileM)
     int32_t col_tiles;   // tiles along N
-    int32_t nunits;      // units along K (>= 1)
-    int32_t cost_full;   // cost of one unit of a tile with tile_rows rows
-    int32_t cost_last;   // cost of one unit of the last row tile
+    int32_t npairs;      // stage pairs along K (>= 1)
+    int32_t cost_full;   // cost of one pair of a tile with tile_rows rows
+    int32_t cost_last;   // cost of one pair of the last row tile
     int32_t pad_;
     int64_t strip_cost;  // cost of one column strip (all row tiles with heads)
     int64_t cost_begin;  // cost before this group's first tile
@@ -128,54 +123,56 @@ struct LaunchArgs {
     uint32_t *control;
     int32_t spin_limit;  // flag polls before a missing part is recomputed instead
     // Workgroup w's range is the cost interval (cut[w], cut[w + 1]]: the
-    // units whose end cost lies in it belong to w (cut[0] = 0, cut[num_wg] =
+    // pairs whose end cost lies in it belong to w (cut[0] = 0, cut[num_wg] =
     // total_cost, non-decreasing; chosen on the host)
     int64_t cut[kMaxWorkgroups + 1];
-    // workgroup w's first tile and unit (pack_start), found by the host
+    // workgroup w's first tile and pair (pack_start), found by the host
     uint64_t start[kMaxWorkgroups];
 };
 
-__host__ __device__ inline int unit_cost(int nrb, int nunits)
+__host__ __device__ inline int pair_cost(int nrb, int npairs)
 {
-    return kCostRowBlock * nrb + kCostFixed + (kCostSpread + nunits - 1) / nunits;
+    return kCostRowBlock * nrb + kCostFixed + (kCostSpread + npairs - 1) / npairs;
 }
 
-// Position of one tile and of a unit in it.
+__host__ __device__ inline int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Position of one tile and of a pair in it.
 struct TilePos {
     int g, strip, rt;       // group, column strip, row tile
-    int unit;               // first unit of interest
+    int pair;               // first pair of interest
     int64_t cost_begin;     // cost where the tile (its head) starts
-    int ucost;              // cost of each of its units
-    int nrb;                // 32-row blocks of the tile
+    int pcost;              // cost of each of its pairs
+    int nrb;                // 16-row blocks of the tile
 };
 
 __host__ __device__ inline int tile_nrb(const GroupArgs &G, int rt)
 {
     const int rows = G.m - rt * G.tile_rows < G.tile_rows ? G.m - rt * G.tile_rows : G.tile_rows;
-    return (rows + kBlockM - 1) / kBlockM;
+    return (rows + 15) >> 4;
 }
 
-// First unit of a tile starting at cost `start` (units of cost uc) whose
-// end cost is > x; nunits when there is none.
-__host__ __device__ inline int first_unit_ending_after(int64_t start, int uc, int nunits, int64_t x)
+// First pair of a tile starting at cost `start` (pairs of cost pc) whose
+// end cost is > x; npairs when there is none.
+__host__ __device__ inline int first_pair_ending_after(int64_t start, int pc, int npairs, int64_t x)
 {
-    const int64_t off = x - start - kCostHead;     // unit j ends at (j + 1) uc
+    const int64_t off = x - start - kCostHead;     // pair j ends at (j + 1) pc
     if (off < 0)
         return 0;
-    const int64_t j = off / uc;
-    return (int)(j < nunits ? j : nunits);
+    const int64_t j = off / pc;
+    return (int)(j < npairs ? j : npairs);
 }
 
 __host__ __device__ inline void finish_pos(const GroupArgs &G, TilePos &p)
 {
-    const int64_t full = kCostHead + (int64_t)G.nunits * G.cost_full;
+    const int64_t full = kCostHead + (int64_t)G.npairs * G.cost_full;
     p.cost_begin = G.cost_begin + p.strip * G.strip_cost + p.rt * full;
-    p.ucost = p.rt == G.row_tiles - 1 ? G.cost_last : G.cost_full;
+    p.pcost = p.rt == G.row_tiles - 1 ? G.cost_last : G.cost_full;
     p.nrb = tile_nrb(G, p.rt);
 }
 
-// The tile holding the first unit whose end cost is > x (g == ng: none).
-inline TilePos locate(const LaunchArgs &args, int64_t x)
+// The tile holding the first pair whose end cost is > x (g == ng: none).
+__host__ __device__ inline TilePos locate(const LaunchArgs &args, int64_t x)
 {
     const GroupArgs *gs = args.g;
     const int ng = args.ng;
@@ -184,6 +181,7 @@ inline TilePos locate(const LaunchArgs &args, int64_t x)
     if (x >= total)
         return p;
     int g = 0;
+#pragma unroll
     for (int i = 1; i < kMaxGroupsPerLaunch; ++i)
         g += args.group_begin[i] <= x ? 1 : 0;
     const GroupArgs &G = gs[g];
@@ -191,16 +189,16 @@ inline TilePos locate(const LaunchArgs &args, int64_t x)
     p.g = g;
     p.strip = (int)(off / G.strip_cost);
     off -= p.strip * G.strip_cost;
-    const int64_t full = kCostHead + (int64_t)G.nunits * G.cost_full;
+    const int64_t full = kCostHead + (int64_t)G.npairs * G.cost_full;
     if (off < (int64_t)(G.row_tiles - 1) * full) {
         p.rt = (int)(off / full);
-        p.unit = first_unit_ending_after(p.rt * full, G.cost_full, G.nunits, off);
+        p.pair = first_pair_ending_after(p.rt * full, G.cost_full, G.npairs, off);
     } else {
         p.rt = G.row_tiles - 1;
-        p.unit = first_unit_ending_after((int64_t)(G.row_tiles - 1) * full, G.cost_last, G.nunits, off);
+        p.pair = first_pair_ending_after((int64_t)(G.row_tiles - 1) * full, G.cost_last, G.npairs, off);
     }
-    if (p.unit >= G.nunits) {        // no unit of this tile ends after x: start at the next tile
-        p.unit = 0;
+    if (p.pair >= G.npairs) {        // no pair of this tile ends after x: start at the next tile
+        p.pair = 0;
         if (++p.rt == G.row_tiles) {
             p.rt = 0;
             if (++p.strip == G.col_tiles) {
@@ -216,10 +214,10 @@ inline TilePos locate(const LaunchArgs &args, int64_t x)
     return p;
 }
 
-// The tile after p (unit 0); g == ng past the last tile.
+// The tile after p (pair 0); g == ng past the last tile.
 __host__ __device__ inline TilePos next_tile(const GroupArgs *gs, int ng, int64_t total, TilePos p)
 {
-    p.unit = 0;
+    p.pair = 0;
     if (++p.rt == gs[p.g].row_tiles) {
         p.rt = 0;
         if (++p.strip == gs[p.g].col_tiles) {
@@ -234,13 +232,13 @@ __host__ __device__ inline TilePos next_tile(const GroupArgs *gs, int ng, int64_
     return p;
 }
 
-// A tile position packed into 64 bits: unit [0, 20), row tile [20, 38),
+// A tile position packed into 64 bits: pair [0, 20), row tile [20, 38),
 // column strip [38, 58), group [58, 64) (63: no tile).
 __host__ __device__ inline uint64_t pack_start(const TilePos &p, int ng)
 {
     if (p.g >= ng)
         return 63ull << 58;
-    return (uint64_t)p.unit | (uint64_t)p.rt << 20 | (uint64_t)p.strip << 38 | (uint64_t)p.g << 58;
+    return (uint64_t)p.pair | (uint64_t)p.rt << 20 | (uint64_t)p.strip << 38 | (uint64_t)p.g << 58;
 }
 
 __host__ __device__ inline TilePos unpack_start(const LaunchArgs &args, uint64_t v)
@@ -254,15 +252,15 @@ __host__ __device__ inline TilePos unpack_start(const LaunchArgs &args, uint64_t
     return p;
 }
 
-// Units [*ub, *ue) of the tile at p whose end cost lies in (lo, hi].
-__host__ __device__ inline void units_in(const TilePos &p, int nunits, int64_t lo, int64_t hi, int &ub, int &ue)
+// Pairs [*pb, *pe) of the tile at p whose end cost lies in (lo, hi].
+__host__ __device__ inline void pairs_in(const TilePos &p, int npairs, int64_t lo, int64_t hi, int &pb, int &pe)
 {
-    ub = first_unit_ending_after(p.cost_begin, p.ucost, nunits, lo);
-    ue = first_unit_ending_after(p.cost_begin, p.ucost, nunits, hi);
+    pb = first_pair_ending_after(p.cost_begin, p.pcost, npairs, lo);
+    pe = first_pair_ending_after(p.cost_begin, p.pcost, npairs, hi);
 }
 
-// Bytes of one workgroup's partial-sum slot: [wave][row block][cb][lane] f32x16.
-constexpr uint32_t kPartialSlot = kWaves * kRowBlocks * 2u * 64u * 64u;
+// Bytes of one workgroup's partial-sum slot: [wave][row block][cb][lane] f32x4.
+constexpr uint32_t kPartialSlot = kWaves * kRowBlocks * 2u * 64u * 16u;
 
 // ---------------------------------------------------------------- device --
 
@@ -270,74 +268,104 @@ constexpr uint32_t kPartialSlot = kWaves * kRowBlocks * 2u * 64u * 64u;
 // eight exact fp16 values.  The convert instruction applies a power-of-two
 // scale only, so it runs with 1.0 and the E4M3 scale is applied by a packed
 // f16 multiply (exact: <= 6 significant bits, result in the normal range).
-__device__ __forceinline__ f16x8 decode8(uint32_t codes, _Float16 s)
+__device__ __forceinline__ f16x8 decode8(uint32_t codes, f16x2 s)
 {
-    const f16x2 ss = {s, s};
-    const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * ss;
-    const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * ss;
-    const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * ss;
-    const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * ss;
-    const f16x8 r = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+    f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * s;
+    f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * s;
+    f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * s;
+    f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * s;
+    f16x8 r = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
     return r;
 }
 
-// The two E4M3FN scale bytes in the low half of a dword -> an fp16 pair.
+// Two E4M3FN scale bytes (low 16 bits) -> fp16 pair.
 __device__ __forceinline__ f16x2 scales2(uint32_t bytes)
 {
     return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bytes, 1.0f, false);
 }
 
+__device__ __forceinline__ f16x2 bcast(_Float16 x)
+{
+    f16x2 r = {x, x};
+    return r;
+}
+
 // ---- LDS layout ----------------------------------------------------------
-// Each wave owns kRing stage slots of kSlotBytes.  A slot holds what the
-// wave fetched for one 64-k stage (lane l's bytes at size * l):
-//   A codes  [row block][lane] x 16 B  (row 32 rb + lane % 32, k 32 (lane / 32) + [0, 32))
-//   B codes  [cb][lane] x 16 B        (column 64 w + 32 cb + lane % 32)
-//   A scales [r][rb] x 4 B             (the stage's four scale bytes of row 32 rb + r)
-//   B scales [r][cb] x 4 B             (likewise for column 64 w + 32 cb + r)
-// After a segment the ring is free and its first 4 KiB serve as the wave's
-// staging area for the transposed fp16 output.
-constexpr uint32_t kSlotACodes = 0;
-constexpr uint32_t kSlotBCodes = kSlotACodes + kRowBlocks * 1024u;
-constexpr uint32_t kSlotAScales = kSlotBCodes + 2u * 1024u;
-constexpr uint32_t kSlotBScales = kSlotAScales + kTileM * 4u;
-constexpr uint32_t kSlotBytes = kSlotBScales + kWaveCols * 4u;
-constexpr uint32_t kWaveRing = kRing * kSlotBytes;
-constexpr uint32_t kLdsBytes = kWaves * kWaveRing;
-static_assert(kLdsBytes <= 160u * 1024u, "LDS budget of one CU");
+// [0, 64 KiB): decoded A operand fragments of two stages,
+//              [stage][row block][MFMA step][lane] x 16 bytes.
+// then kRing raw code stages, each holding what every wave fetched for one
+// stage (lane l's 16 bytes at 16 l):
+//   A codes  [wave][lane] x 16 B   (the rows of the wave's A-decode role)
+//   B codes  [wave][cb][lane] x 16 B   (the wave's own 32 columns)
+// then two scale windows, each holding the scale bytes of two consecutive
+// stages (16 bytes per row, fetched by lanes 0..15, one row each):
+//   A scales [wave][16 rows] x 16 B,  B scales [wave][cb][16 rows] x 16 B
+// then two counters of decoded A halves (MFMA steps 0-1 and 2-3) that
+// order the waves' shared use of the A operand buffers.
+constexpr int kRing = 3;
+constexpr uint32_t kLdsAOps = 2u * kRowBlocks * 4u * 64u * 16u;
+constexpr uint32_t kRawACodes = 0;
+constexpr uint32_t kRawBCodes = kRawACodes + kWaves * 1024u;
+constexpr uint32_t kRawStage = kRawBCodes + kWaves * 2u * 1024u;
+constexpr uint32_t kWinAScales = 0;
+constexpr uint32_t kWinBScales = kWinAScales + kWaves * 256u;
+constexpr uint32_t kWindow = kWinBScales + kWaves * 2u * 256u;
+constexpr uint32_t kLdsWindows = kLdsAOps + kRing * kRawStage;
+constexpr uint32_t kLdsSync = kLdsWindows + 2u * kWindow;
+constexpr uint32_t kLdsBytes = kLdsSync + 16u;
+// Loads a wave issues: kCodeLoads code loads every stage, kScaleLoads
+// scale loads every odd stage (after its code loads, for the pair starting
+// three stages on).  With kRing = 3 stages in flight, at the top of every
+// stage c exactly kWaitAfterNext loads have been issued after the last load
+// that stage c + 1 needs: the codes of c + 1 when c is even, the scale
+// window of the pair starting at c + 1 when c is odd.
+constexpr int kCodeLoads = 3;
+constexpr int kScaleLoads = 2;
+constexpr int kWaitAfterNext = 2 * kCodeLoads + kScaleLoads;
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 // Buffer resource over `bytes` bytes at `p` (raw buffer, no stride); reads
 // past the end return zero.
 __device__ __forceinline__ i32x4 rsrc(const void *p, uint32_t bytes)
 {
     const uint64_t a = (uint64_t)(uintptr_t)p;
-    const i32x4 r = {(int32_t)(uint32_t)a, (int32_t)(uint32_t)(a >> 32) & 0xFFFF, (int32_t)bytes, 0x00020000};
+    i32x4 r = {(int32_t)(uint32_t)a, (int32_t)(uint32_t)(a >> 32) & 0xFFFF, (int32_t)bytes, 0x00020000};
     return r;
 }
 
-// Direct HBM -> LDS load: lane l's 16 (or 4) bytes at voff + soff land at
-// LDS byte lds + 16 l (4 l); a buffer resource reads 0 past its end.  The
-// load is issued from inline assembly that sets m0 (the LDS address) and
-// restores it, so the compiler neither loses a value it keeps in m0 nor
-// sees an LDS write it would have to wait for before every later LDS read
-// (it cannot tell the ring slots apart).  Callers wait for these loads
-// with an explicit vmcnt before reading what they wrote.
-__device__ __forceinline__ void dma16(i32x4 rs, uint32_t lds, uint32_t voff, uint32_t soff)
+// Direct HBM -> LDS loads: lane l's 16 bytes at voff + soff land at LDS
+// byte lds + 16 l.  Issued from inline assembly that sets m0 (the LDS
+// address) and restores it, so the compiler neither loses a value it keeps
+// in m0 nor orders later LDS reads behind these writes (it cannot tell the
+// ring slots apart); callers wait with an explicit vmcnt before reading.
+__device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, i32x4 rs, uint32_t soff)
 {
     uint32_t saved;
     asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
                  "buffer_load_dwordx4 %2, %3, %4 offen lds\n\ts_mov_b32 m0, %0"
                  : "=&s"(saved) : "s"(lds), "v"(voff), "s"(rs), "s"(soff) : "memory");
 }
-__device__ __forceinline__ void dma4(i32x4 rs, uint32_t lds, uint32_t voff, uint32_t soff)
+// The same for lanes 0..15 only (exec narrowed and restored inside the asm,
+// so the compiler sees no divergent branch around a load it cannot see).
+__device__ __forceinline__ void dma16_lanes16(uint32_t lds, uint32_t voff, i32x4 rs, uint32_t soff)
 {
-    uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-                 "buffer_load_dword %2, %3, %4 offen lds\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved) : "s"(lds), "v"(voff), "s"(rs), "s"(soff) : "memory");
+    uint64_t saved;
+    uint32_t saved_m0;
+    asm volatile("s_mov_b64 %0, exec\n\ts_mov_b64 exec, 0xffff\n\ts_mov_b32 %1, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+                 "buffer_load_dwordx4 %3, %4, %5 offen lds\n\ts_mov_b32 m0, %1\n\ts_mov_b64 exec, %0"
+                 : "=&s"(saved), "=&s"(saved_m0) : "s"(lds), "v"(voff), "s"(rs), "s"(soff) : "memory");
 }
-
-// s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding), not
-// moved across by the scheduler.
+// The same for lanes 0..31.
+__device__ __forceinline__ void dma16_lanes32(uint32_t lds, uint32_t voff, i32x4 rs, uint32_t soff)
+{
+    uint64_t saved;
+    uint32_t saved_m0;
+    asm volatile("s_mov_b64 %0, exec\n\ts_mov_b64 exec, 0xffffffff\n\ts_mov_b32 %1, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+                 "buffer_load_dwordx4 %3, %4, %5 offen lds\n\ts_mov_b32 m0, %1\n\ts_mov_b64 exec, %0"
+                 : "=&s"(saved), "=&s"(saved_m0) : "s"(lds), "v"(voff), "s"(rs), "s"(soff) : "memory");
+}
+// s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt()
 {
@@ -357,169 +385,280 @@ __device__ __forceinline__ int lane_id()
     return l;
 }
 
-// Raw codes and scale bytes of one stage, as one lane holds them.
-template <int NRB>
-struct StageRaw {
-    u32x4 a[NRB];   // dword s: the eight codes of MFMA step s, per row block
-    u32x4 b[2];     // likewise per column block
-    u32x4 sa;       // dword rb: scale bytes of row 32 rb + r (bytes 2h, 2h + 1 are this lane's)
-    u32x2 sb;       // dword cb: scale bytes of column 32 cb + r
-};
+// The decoded A operands are the only LDS data the waves share inside the
+// stage loop (codes and scales are wave-private DMA targets).  Instead of a
+// workgroup barrier per stage, counter h (h = 0: MFMA steps 0-1, h = 1:
+// steps 2-3) counts the waves that have written their part of those steps
+// for the next stage.  Before a wave reads half h of stage c it waits until
+// every wave has written it (count >= waves * (c - first stage)); every wave
+// writes half h of stage c + 1 only after reading half h of stage c - 1,
+// which shares its buffer, so the same wait also keeps the writes of stage
+// c + 1 from overtaking a slower wave's reads of stage c - 1.  LDS performs
+// a wave's operations in issue order, so a count is added only after the
+// wave's writes.  Waves thus drift up to a stage apart, and one wave's
+// decode overlaps another's MFMAs.  The wait is bounded (a broken count
+// gives wrong sums instead of a hang).
+constexpr int kSyncSpinLimit = 1 << 14;
+// Both are single asm statements so that the hot loop stays one basic
+// block for the compiler; the LDS operations they add only make the
+// compiler's own (in-order) LDS waits more conservative.
+// `pre` is the counter as read some MFMA steps earlier by a plain LDS load:
+// the counter only grows, so if that value already meets the target the
+// wait ends without a new read (whose lgkmcnt(0) would drain every LDS
+// operation in flight), and the compiler's wait for `pre` covers only the
+// LDS operations issued before it.
+__device__ __forceinline__ void half_wait(uint32_t count_addr, int target, int pre)
+{
+    int v;
+    int seen, left = kSyncSpinLimit;
+    asm volatile("v_readfirstlane_b32 %1, %5\n\t"
+                 "s_cmp_ge_i32 %1, %4\n\t"
+                 "s_cbranch_scc1 2f\n"
+                 "1:\n\t"
+                 "ds_read_b32 %0, %3\n\t"
+                 "s_waitcnt lgkmcnt(0)\n\t"
+                 "v_readfirstlane_b32 %1, %0\n\t"
+                 "s_cmp_ge_i32 %1, %4\n\t"
+                 "s_cbranch_scc1 2f\n\t"
+                 "s_sleep 1\n\t"
+                 "s_sub_i32 %2, %2, 1\n\t"
+                 "s_cmp_gt_i32 %2, 0\n\t"
+                 "s_cbranch_scc1 1b\n"
+                 "2:"
+                 : "=&v"(v), "=&s"(seen), "+s"(left)
+                 : "v"(count_addr), "s"(target), "v"(pre)
+                 : "memory", "scc");
+}
+// Early read of a counter for half_wait (a volatile LDS load, so it stays
+// where it is issued relative to the other LDS operations).
+typedef __attribute__((address_space(3))) const volatile int lds_cvint;
+__device__ __forceinline__ int count_read(uint32_t count_addr)
+{
+    return *reinterpret_cast<lds_cvint *>((uintptr_t)count_addr);
+}
+__device__ __forceinline__ void half_done(uint32_t count_addr, uint32_t one)
+{
+    uint64_t saved;
+    asm volatile("s_mov_b64 %0, exec\n\t"
+                 "s_mov_b64 exec, 1\n\t"
+                 "ds_add_u32 %1, %2\n\t"
+                 "s_mov_b64 exec, %0"
+                 : "=&s"(saved)
+                 : "v"(count_addr), "v"(one)
+                 : "memory");
+}
 
-// Stage units [ub, ue) of one output tile with NRB row blocks (compile time,
-// so the hot loop has no branches), added into `outer`.  The tile is rows
-// [m0, m0 + 32 NRB) and columns [n0, n0 + 256) of one group; wave `wave`
-// owns columns n0 + 64 wave + [0, 64).  Lane (r, h) of the wave holds
-// outer[i][cb][v] = C[m0 + 32 i + 8 (v / 4) + 4 h + v % 4][n0 + 64 wave + 32 cb + r].
-template <int NRB>
+// Stage pairs [pb, pe) of one output tile with NRB row blocks (compile
+// time, so the hot loop has no branches), added into `outer`.  W waves; the
+// tile is rows [m0, m0 + 16 NRB) and columns [n0, n0 + 32 W) of one group.
+// Lane (r, q) of wave w holds outer[i][cb][e] = C[m0 + 16i + 4q + e][n0 + 32w + 16cb + r].
+template <int NRB, int W>
 __device__ __forceinline__ void segment(const GroupArgs &G, int m0, int n0, int wave, uint8_t *smem,
-                                        int ub, int ue, f32x16 (&outer)[NRB][2])
+                                        int pb, int pe, f32x4 (&outer)[NRB][2])
 {
     const int M = G.m, N = G.n, K = G.k;
     const int lane = lane_id();
-    const int r = lane & 31, h = lane >> 5;
+    const int r = lane & 15, q = lane >> 4;
     const uint32_t row_bytes = (uint32_t)K >> 1, row_scales = (uint32_t)K >> 4;
-    const int nstages = K / kStageK;
-    const int c_begin = ub * kStagesPerUnit;
-    const int c_end = min(ue * kStagesPerUnit, nstages);
-    if (c_begin >= c_end)
-        return;
+    const int nstages = (K + kStageK - 1) / kStageK;
+    const int c_begin = 2 * pb, c_end = min(2 * pe, (nstages + 1) & ~1);
 
+    if (c_begin < c_end) {
     const i32x4 ra_codes = rsrc(G.a, (uint32_t)M * row_bytes);
     const i32x4 ra_scales = rsrc(G.sfa, (uint32_t)M * row_scales);
     const i32x4 rb_codes = rsrc(G.b, (uint32_t)N * row_bytes);
     const i32x4 rb_scales = rsrc(G.sfb, (uint32_t)N * row_scales);
-    uint8_t *ring = smem + wave * kWaveRing;
-    const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
 
-    // Per-lane byte offsets of what the lane fetches each stage (the stage
-    // adds its k offset as the scalar offset).  Rows past M and columns past
-    // N lie past the resource's end and read as 0.
-    uint32_t voff_a[NRB], voff_b[2], voff_sa[2], voff_sb;
+    // A decode role: wave w decodes row block w % NRB (all four MFMA steps).
+    // For NRB < W several waves decode the same block and store identical
+    // bytes, which keeps the hot loop free of branches.
+    const int a_rb = wave % NRB;
+    const uint32_t arow = (uint32_t)min(m0 + 16 * a_rb + r, M - 1);
+    // Lane (r, q) covers k0 + 32q + [0, 32): 16 code bytes at k0/2 + 16q and
+    // the two scale bytes at k0/16 + 2q of its row.
+    const uint32_t a_voff = arow * row_bytes + 16u * q;
+    const uint32_t sa_voff = arow * row_scales;
+    uint32_t b_voff[2], sb_voff[2];
+    // B scale rows for one 32-lane load: lane 16 cb + r fetches column block
+    // cb's row r (lanes 32..63 are masked off)
+    const uint32_t sb_voff32 = (uint32_t)min(n0 + 32 * wave + 16 * (q & 1) + r, N - 1) * row_scales;
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb)
-        voff_a[rb] = ((uint32_t)(m0 + kBlockM * rb + r)) * row_bytes + 16u * (uint32_t)h;
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-        voff_b[cb] = ((uint32_t)(n0 + kWaveCols * wave + 32 * cb + r)) * row_bytes + 16u * (uint32_t)h;
-    // A scales: load i, lane l fetches row 32 (l % 4) + 16 i + l / 4, landing at [r][rb]
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-        voff_sa[i] = ((uint32_t)(m0 + 32 * (lane & 3) + 16 * i + (lane >> 2))) * row_scales;
-    // B scales: lane l fetches column 32 (l % 2) + l / 2, landing at [r][cb]
-    voff_sb = ((uint32_t)(n0 + kWaveCols * wave + 32 * (lane & 1) + (lane >> 1))) * row_scales;
+    for (int cb = 0; cb < 2; ++cb) {
+        const uint32_t col = (uint32_t)min(n0 + 32 * wave + 16 * cb + r, N - 1);
+        b_voff[cb] = col * row_bytes + 16u * q;
+        sb_voff[cb] = col * row_scales;
+    }
+    const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
+    const uint32_t raw_base = smem_base + kLdsAOps;
+    int *sync = reinterpret_cast<int *>(smem + kLdsSync);
+    const uint32_t sync_addr = smem_base + kLdsSync;
+    const uint32_t one = 1u;
+    f16x8 *lds_a = reinterpret_cast<f16x8 *>(smem);            // [2][kRowBlocks][4][64]
+    auto aop = [&](int buf, int rb, int s) -> f16x8 & {
+        return lds_a[((buf * kRowBlocks + rb) * 4 + s) * 64 + lane];
+    };
 
-    // Fetch stage c (clamped to the group's last stage, so the number of
-    // loads in flight never depends on K) into ring slot `slot`: NRB + 2
-    // code loads and 3 scale loads.
-    auto fetch = [&](int c, int slot) {
+    f32x4 inner[NRB][2];
+    f16x8 bf[2][4];     // decoded B operands of the current stage, per MFMA step
+    f16x8 af[NRB];
+
+    // Codes of stage c (clamped to the last stage, so the number of loads in
+    // flight never depends on K) into ring slot c % kRing.
+    auto fetch_codes = [&](int c) {
         const uint32_t k0 = (uint32_t)min(c, nstages - 1) * kStageK;
-        const uint32_t s = ring_lds + (uint32_t)slot * kSlotBytes;
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb)
-            dma16(ra_codes, s + kSlotACodes + rb * 1024u, voff_a[rb], k0 >> 1);
+        const uint32_t slot = raw_base + (uint32_t)(c % kRing) * kRawStage;
+        dma16(slot + kRawACodes + wave * 1024u, a_voff, ra_codes, k0 >> 1);
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
-            dma16(rb_codes, s + kSlotBCodes + cb * 1024u, voff_b[cb], k0 >> 1);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-            dma4(ra_scales, s + kSlotAScales + 256u * i, voff_sa[i], k0 >> 4);
-        dma4(rb_scales, s + kSlotBScales, voff_sb, k0 >> 4);
+            dma16(slot + kRawBCodes + (wave * 2 + cb) * 1024u, b_voff[cb], rb_codes, k0 >> 1);
     };
-    constexpr int kLoadsPerStage = NRB + 5;
-    // at the top of stage c the loads of stages c + 2 .. c + kRing - 1 may
-    // still be in flight; those of stage c + 1 must have landed
-    constexpr int kWaitNext = (kRing - 2) * kLoadsPerStage;
-
-    auto read_raw = [&](int slot) -> StageRaw<NRB> {
-        const uint8_t *s = ring + slot * kSlotBytes;
-        const int l = lane_id();
-        StageRaw<NRB> v;
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb)
-            v.a[rb] = reinterpret_cast<const u32x4 *>(s + kSlotACodes + rb * 1024)[l];
+    // Scale window w (stages 2w and 2w + 1: 16 bytes of each row) into window
+    // buffer w % 2, fetched by lanes 0..15 (row r = lane).
+    auto fetch_scales = [&](int w) {
+        const uint32_t sk = (uint32_t)min(w, (nstages - 1) >> 1) * (2u * kStageK / 16u);
+        const uint32_t win = smem_base + kLdsWindows + (uint32_t)(w & 1) * kWindow;
+        dma16_lanes16(win + kWinAScales + wave * 256u, sa_voff, ra_scales, sk);
+        dma16_lanes32(win + kWinBScales + wave * 2 * 256u, sb_voff32, rb_scales, sk);
+    };
+    auto raw_slot = [&](int c) -> const uint8_t * {
+        return smem + kLdsAOps + (uint32_t)(c % kRing) * kRawStage;
+    };
+    // The scale dword holding lane (r, q)'s two scale bytes of stage c: row r,
+    // byte 8 (c % 2) + 2q of window c / 2 (returned shifted into the low half).
+    auto read_scales = [&](int c, uint32_t &sa, uint32_t (&sb)[2]) {
+        const uint8_t *win = smem + kLdsWindows + (uint32_t)((c >> 1) & 1) * kWindow;
+        const uint32_t off = 16u * r + 8u * (c & 1) + 4u * (q >> 1);
+        const uint32_t sh = 16u * (q & 1);
+        sa = *reinterpret_cast<const uint32_t *>(win + kWinAScales + wave * 256u + off) >> sh;
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
-            v.b[cb] = reinterpret_cast<const u32x4 *>(s + kSlotBCodes + cb * 1024)[l];
-        v.sa = reinterpret_cast<const u32x4 *>(s + kSlotAScales)[l & 31];
-        v.sb = reinterpret_cast<const u32x2 *>(s + kSlotBScales)[l & 31];
-        return v;
+            sb[cb] = *reinterpret_cast<const uint32_t *>(win + kWinBScales + (wave * 2 + cb) * 256u + off) >> sh;
+    };
+    auto a_codes = [&](const uint8_t *slot) -> u32x4 {
+        return reinterpret_cast<const u32x4 *>(slot + kRawACodes + wave * 1024u)[lane];
+    };
+    auto b_codes = [&](const uint8_t *slot, int cb) -> u32x4 {
+        return reinterpret_cast<const u32x4 *>(slot + kRawBCodes + (wave * 2 + cb) * 1024u)[lane];
+    };
+    // The two scales of a raw block of stage c as fp16; zero for lanes whose
+    // 32 k lie past K (K % 64 == 0: a lane's 32 k are all in or all out).
+    auto scales_of = [&](uint32_t two, int c) -> f16x2 {
+        const bool valid = c * kStageK + 32 * q < K;
+        return scales2(valid ? two : 0u);
+    };
+    // Operand of MFMA step s (k = 32q + 8s + [0, 8)) from its code dword.
+    auto operand = [&](uint32_t codes, f16x2 sc, int s) -> f16x8 {
+        return decode8(codes, bcast(sc[s >> 1]));
+    };
+    auto decode_a_into = [&](const u32x4 &codes, f16x2 sc, int buf, int s) {
+        aop(buf, a_rb, s) = operand(codes[s], sc, s);
     };
 
-    // Per-stage fp16 scales of this lane: [0] for steps 0-1, [1] for steps 2-3.
-    struct Scales {
-        f16x2 a[NRB];
-        f16x2 b[2];
-    };
-    auto scales_of = [&](const StageRaw<NRB> &v) -> Scales {
-        Scales sc;
-        const uint32_t sh = 16u * (uint32_t)h;
+    // prologue: stages c_begin .. c_begin + 2 in flight; c_begin decoded (A to
+    // LDS buffer 0, B to bf)
+    // Issue order keeps exactly kWaitAfterNext loads behind the codes of
+    // stage c + 1 at the top of every stage c, this first one included.
+    fetch_scales(c_begin >> 1);
+    fetch_codes(c_begin);
+    fetch_codes(c_begin + 1);
+    fetch_scales((c_begin >> 1) + 1);
+    fetch_codes(c_begin + 2);
+    wait_vmcnt<kWaitAfterNext>();
+    {
+        const uint8_t *slot = raw_slot(c_begin);
+        uint32_t sa, sb[2];
+        read_scales(c_begin, sa, sb);
+        const f16x2 sca = scales_of(sa, c_begin);
+        const u32x4 ac = a_codes(slot);
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb)
-            sc.a[rb] = scales2(v.sa[rb] >> sh);
+        for (int s = 0; s < 4; ++s)
+            decode_a_into(ac, sca, 0, s);
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-            sc.b[cb] = scales2(v.sb[cb] >> sh);
-        return sc;
-    };
+        for (int cb = 0; cb < 2; ++cb) {
+            const f16x2 sc = scales_of(sb[cb], c_begin);
+            const u32x4 bc = b_codes(slot, cb);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                bf[cb][s] = operand(bc[s], sc, s);
+        }
+    }
+    if (threadIdx.x < 2)
+        sync[threadIdx.x] = 0;     // no wave counts again before this barrier
+    __syncthreads();
+    int pre0 = 0;       // early read of counter 0 for the next stage (the first stage needs none)
 
-    f32x16 inner[NRB][2];
-    f16x8 da[2][NRB], db[2][2];     // decoded operands of two MFMA steps
-
-    auto decode_step = [&](const StageRaw<NRB> &v, const Scales &sc, int s, f16x8 (&oa)[NRB], f16x8 (&ob)[2]) {
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb)
-            oa[rb] = decode8(v.a[rb][s], sc.a[rb][s >> 1]);
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-            ob[cb] = decode8(v.b[cb][s], sc.b[cb][s >> 1]);
-    };
-
-    // prologue: stages c_begin .. c_begin + kRing - 2 in flight, stage
-    // c_begin read and its step 0 decoded
-#pragma unroll
-    for (int i = 0; i < kRing - 1; ++i)
-        fetch(c_begin + i, i);
-    wait_vmcnt<kWaitNext>();
-    StageRaw<NRB> cur = read_raw(0);
-    Scales sc = scales_of(cur);
-    decode_step(cur, sc, 0, da[0], db[0]);
-    int slot = 0;                   // ring slot of the current stage
-
-    // Stage c: fetch stage c + kRing - 1 into the slot stage c - 1 used (read
-    // one stage ago); per MFMA step s: 2 NRB MFMAs on the operands of step s,
-    // then decode step s + 1 (at s = 3: step 0 of stage c + 1, whose raw
-    // codes are read from the ring at the start of step 3, once stage c's
-    // codes are all decoded and their registers are free).
-    auto stage = [&](int c, auto first_t) {
+    // Stage c: fetch the codes of stage c + 3 into the ring slot stage c used
+    // (and, on odd stages, the scale window of stages c + 3 and c + 4 into the
+    // window buffer the stages before c used); wait for stage c + 1; per MFMA step s: 2 * NRB MFMAs on the A fragments of step s
+    // (read from LDS; a row block's fragment for step s + 1 is read right
+    // after its last use), then step s of B (stage c + 1) is decoded into the
+    // freed bf slot and step s of A (stage c + 1) into the other LDS buffer
+    // (step 0 of A right after the top-of-stage reads, which it covers).
+    // Each half of stage c's A is read only after every wave has written it
+    // (half_wait), and each written half of stage c + 1 is counted
+    // (half_done).  The last stage decodes unused data instead of branching.
+    auto stage = [&](int c, auto buf_t, auto first_t) {
+        constexpr int kBuf = decltype(buf_t)::value;
         constexpr bool kFirst = decltype(first_t)::value;   // first stage after a fold: MFMA sums restart
-        const int fslot = slot == 0 ? kRing - 1 : slot - 1;
-        const int nslot = slot == kRing - 1 ? 0 : slot + 1;
-        fetch(c + kRing - 1, fslot);
-        StageRaw<NRB> nxt;
-        Scales nsc;
+        constexpr int kNext = 1 - kBuf;
+        fetch_codes(c + 3);
+        if (kBuf == 1)
+            fetch_scales((c + 3) >> 1);
+        wait_vmcnt<kWaitAfterNext>();
+        const uint8_t *nslot = raw_slot(c + 1);
+        uint32_t sa, sb[2];
+        read_scales(c + 1, sa, sb);
+        const f16x2 sa_next = scales_of(sa, c + 1);
+        f16x2 sb_next[2];
+        u32x4 bc_next[2];
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+            sb_next[cb] = scales_of(sb[cb], c + 1);
+            bc_next[cb] = b_codes(nslot, cb);
+        }
+        const u32x4 ac_next = a_codes(nslot);
+        const int ready = __builtin_amdgcn_readfirstlane(kWaves * (c - c_begin));
+        half_wait(sync_addr, ready, pre0);
+#pragma unroll
+        for (int i = 0; i < NRB; ++i)
+            af[i] = aop(kBuf, i, 0);
+        // step 0 of the next stage's A while this stage's step-0 reads land
+        decode_a_into(ac_next, sa_next, kNext, 0);
+        int pre1 = 0;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            if (s == 3) {
-                wait_vmcnt<kWaitNext>();
-                nxt = read_raw(nslot);
-            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (s == 1)
+                half_wait(sync_addr + 4u, ready, pre1);   // step 2's fragments are read during step 1
 #pragma unroll
-            for (int i = 0; i < NRB; ++i)
+            for (int i = 0; i < NRB; ++i) {
 #pragma unroll
                 for (int cb = 0; cb < 2; ++cb)
-                    inner[i][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                        da[s & 1][i], db[s & 1][cb], (kFirst && s == 0) ? f32x16{} : inner[i][cb], 0, 0, 0);
-            if (s < 3) {
-                decode_step(cur, sc, s + 1, da[(s + 1) & 1], db[(s + 1) & 1]);
-            } else {
-                nsc = scales_of(nxt);
-                decode_step(nxt, nsc, 0, da[0], db[0]);
+                    inner[i][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        af[i], bf[cb][s], (kFirst && s == 0) ? f32x4{0.f, 0.f, 0.f, 0.f} : inner[i][cb], 0, 0, 0);
+                if (s < 3)
+                    af[i] = aop(kBuf, i, s + 1);
+                // early counter reads, half a step (second half of this
+                // stage's A) or one and a half steps (first half of the next
+                // stage's A) before they are checked
+                if (i == (NRB - 1) / 2) {
+                    if (s == 0)
+                        pre1 = count_read(sync_addr + 4u);
+                    else if (s == 3)
+                        pre0 = count_read(sync_addr);
+                }
             }
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
+                bf[cb][s] = operand(bc_next[cb][s], sb_next[cb], s);
+                asm volatile("" : "+v"(bf[cb][s]));   // keep the decode inside step s
+            }
+            if (s > 0)
+                decode_a_into(ac_next, sa_next, kNext, s);
+            if (s & 1)
+                half_done(sync_addr + 4u * (s >> 1), one);
         }
-        cur = nxt;
-        sc = nsc;
-        slot = nslot;
+        __builtin_amdgcn_sched_barrier(0);
     };
     auto fold = [&]() {
 #pragma unroll
@@ -529,26 +668,39 @@ __device__ __forceinline__ void segment(const GroupArgs &G, int m0, int n0, int 
                 outer[i][cb] += inner[i][cb];
     };
 
+    // Stages alternate the LDS buffer; the MFMA sums are folded into `outer`
+    // every kFoldStages stages (and after a last lone pair).  An odd stage
+    // count gets one extra stage whose scales are all zero (its k lie past
+    // K), so the loop body has no branch.
+    static_assert(kFoldStages == 4, "a fold every two stage pairs");
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
     int c = c_begin;
-    while (c < c_end) {
-        stage(c, std::true_type{});
-        ++c;
-        const int n = min(kFoldStages - 1, c_end - c);
-        for (int i = 0; i < n; ++i, ++c)
-            stage(c, std::false_type{});
+    for (; c + 4 <= c_end; c += 4) {
+        stage(c, B0{}, std::true_type{});
+        stage(c + 1, B1{}, std::false_type{});
+        stage(c + 2, B0{}, std::false_type{});
+        stage(c + 3, B1{}, std::false_type{});
         fold();
     }
-    // drain the clamped prefetches before the ring is reused
+    if (c < c_end) {
+        stage(c, B0{}, std::true_type{});
+        stage(c + 1, B1{}, std::false_type{});
+        fold();
+    }
+    // drain the clamped prefetches before the LDS is reused
     wait_vmcnt<0>();
+    __syncthreads();
+    }
 }
 
 // fp16 (round to nearest even) of the tile's sums into C, rows < m0 + rows.
 // Fast path (n % 4 == 0 and c 8-byte aligned, so every group of four
 // columns is wholly inside or outside the matrix): the four lanes of a quad
-// (r = 4t .. 4t + 3) hold rows 8 g + 4 h .. + 3 of four consecutive columns
-// in accumulator elements 4 g .. 4 g + 3, so a 4 x 4 transpose of fp16
-// values across the quad (two DPP exchanges) leaves each lane with four
-// consecutive columns of one row, written as one 8-byte store.
+// (r = 4j .. 4j + 3) hold rows 4q .. 4q + 3 of four consecutive columns, so a
+// 4 x 4 transpose of fp16 values across the quad (two DPP exchanges) leaves
+// each lane with four consecutive columns of one row, written as one 8-byte
+// store instead of four 2-byte ones.
 __device__ __forceinline__ uint32_t quad_swap1(uint32_t x)   // value of lane r ^ 1
 {
     return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);
@@ -560,45 +712,39 @@ __device__ __forceinline__ uint32_t quad_swap2(uint32_t x)   // value of lane r 
 
 template <int NRB>
 __device__ __forceinline__ void store_tile(const GroupArgs &G, int m0, int rows, int n0, int wave,
-                                           const f32x16 (&outer)[NRB][2])
+                                           const f32x4 (&outer)[NRB][2])
 {
     const int lane = lane_id();
-    const int r = lane & 31, h = lane >> 5;
+    const int r = lane & 15, q = lane >> 4;
     _Float16 *C = G.c;
     const int N = G.n;
     if ((N & 3) == 0 && ((uintptr_t)C & 7) == 0) {
-        const int u = r & 3;
-        const bool odd = (u & 1) != 0, hi2 = (u & 2) != 0;
-        // this lane's row within a group of four after the transpose
-        const int row_in = 4 * h + 2 * (u & 1) + (u >> 1);
-        const int col = n0 + kWaveCols * wave + (r & ~3);
+        const bool odd = (r & 1) != 0, hi2 = (r & 2) != 0;
+        // this lane's row and first column after the transpose
+        const int row_in = 4 * q + 2 * (r & 1) + ((r >> 1) & 1);
+        const int col = n0 + 32 * wave + (r & ~3);
 #pragma unroll
         for (int i = 0; i < NRB; ++i) {
+            const int row = m0 + 16 * i + row_in;
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int row = m0 + kBlockM * i + 8 * g + row_in;
-                    const f32x16 &v = outer[i][cb];
-                    const uint32_t p01 =
-                        __builtin_bit_cast(uint32_t, f16x2{(_Float16)v[4 * g], (_Float16)v[4 * g + 1]});
-                    const uint32_t p23 =
-                        __builtin_bit_cast(uint32_t, f16x2{(_Float16)v[4 * g + 2], (_Float16)v[4 * g + 3]});
-                    // step 1: even lanes end with rows +0, +1 and odd lanes with
-                    // rows +2, +3, each for the column pair (r & ~1, +1)
-                    const uint32_t mine = odd ? p23 : p01;
-                    const uint32_t recv = quad_swap1(odd ? p01 : p23);
-                    const uint32_t lo = odd ? recv : mine, hi = odd ? mine : recv;
-                    const uint32_t rowA = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-                    const uint32_t rowB = __builtin_amdgcn_perm(hi, lo, 0x07060302u);
-                    // step 2: lanes r and r ^ 2 swap halves of their column quad
-                    const uint32_t keep = hi2 ? rowB : rowA;
-                    const uint32_t recv2 = quad_swap2(hi2 ? rowA : rowB);
-                    const uint64_t out = hi2 ? ((uint64_t)keep << 32 | recv2) : ((uint64_t)recv2 << 32 | keep);
-                    const int c0 = col + 32 * cb;
-                    if (row < m0 + rows && c0 < N)
-                        *reinterpret_cast<uint64_t *>(C + (size_t)row * N + c0) = out;
-                }
+                const f32x4 v = outer[i][cb];
+                const uint32_t p01 = __builtin_bit_cast(uint32_t, f16x2{(_Float16)v[0], (_Float16)v[1]});
+                const uint32_t p23 = __builtin_bit_cast(uint32_t, f16x2{(_Float16)v[2], (_Float16)v[3]});
+                // step 1: even lanes end with rows 4q, 4q+1 and odd lanes with
+                // rows 4q+2, 4q+3, each for the column pair (r & ~1, +1)
+                const uint32_t mine = odd ? p23 : p01;
+                const uint32_t recv = quad_swap1(odd ? p01 : p23);
+                const uint32_t lo = odd ? recv : mine, hi = odd ? mine : recv;
+                const uint32_t rowA = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+                const uint32_t rowB = __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+                // step 2: lanes r and r ^ 2 swap halves of their column quad
+                const uint32_t keep = hi2 ? rowB : rowA;
+                const uint32_t recv2 = quad_swap2(hi2 ? rowA : rowB);
+                const uint64_t out = hi2 ? ((uint64_t)keep << 32 | recv2) : ((uint64_t)recv2 << 32 | keep);
+                const int c0 = col + 16 * cb;
+                if (row < m0 + rows && c0 < N)
+                    *reinterpret_cast<uint64_t *>(C + (size_t)row * N + c0) = out;
             }
         }
         return;
@@ -607,12 +753,12 @@ __device__ __forceinline__ void store_tile(const GroupArgs &G, int m0, int rows,
     for (int i = 0; i < NRB; ++i) {
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
-            const int col = n0 + kWaveCols * wave + 32 * cb + r;
+            const int col = n0 + 32 * wave + 16 * cb + r;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int row = m0 + kBlockM * i + 8 * (v >> 2) + 4 * h + (v & 3);
+            for (int e = 0; e < 4; ++e) {
+                const int row = m0 + 16 * i + 4 * q + e;
                 if (row < m0 + rows && col < N)
-                    C[(size_t)row * N + col] = (_Float16)outer[i][cb][v];
+                    C[(size_t)row * N + col] = (_Float16)outer[i][cb][e];
             }
         }
     }
@@ -620,7 +766,7 @@ __device__ __forceinline__ void store_tile(const GroupArgs &G, int m0, int rows,
 
 // Partial sums of split tiles.  Slot w (one per workgroup) holds the sums of
 // workgroup w's first segment in the register layout of `outer`:
-// [wave][row block][cb][lane] x f32x16.  They are written and read with
+// [wave][row block][cb][lane] x f32x4.  They are written and read with
 // agent-coherent (sc1) buffer accesses, and the flag with relaxed agent-scope
 // atomics; ordering comes from waiting for the stores (vmcnt) before the flag
 // is set.  No release/acquire fence is used: on gfx950 those write back or
@@ -635,13 +781,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(const LaunchArgs 
 
 __device__ __forceinline__ int partial_base(int slot, int wave)
 {
-    return slot * (int)kPartialSlot + wave * kRowBlocks * 2 * 4096;
+    return slot * (int)kPartialSlot + wave * kRowBlocks * 2 * 1024;
 }
 
 // Producer side: publish the partial sums of this workgroup's first segment.
 template <int NRB>
 __device__ __forceinline__ void publish_partial(const LaunchArgs &args, uint32_t epoch, int slot, int wave,
-                                                const f32x16 (&outer)[NRB][2])
+                                                const f32x4 (&outer)[NRB][2])
 {
     const int lane = lane_id();
     const __amdgpu_buffer_rsrc_t rs = partial_rsrc(args);
@@ -650,13 +796,7 @@ __device__ __forceinline__ void publish_partial(const LaunchArgs &args, uint32_t
     for (int i = 0; i < NRB; ++i)
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const f32x4 v = {outer[i][cb][4 * q], outer[i][cb][4 * q + 1], outer[i][cb][4 * q + 2],
-                                 outer[i][cb][4 * q + 3]};
-                __builtin_amdgcn_raw_buffer_store_b128(v, rs, lane * 16, base + ((i * 2 + cb) * 4 + q) * 1024,
-                                                       kCoherent);
-            }
+            __builtin_amdgcn_raw_buffer_store_b128(outer[i][cb], rs, lane * 16, base + (i * 2 + cb) * 1024, kCoherent);
     wait_vmcnt<0>();               // every store of this wave has reached the coherence point
     __syncthreads();
     if (threadIdx.x == 0)
@@ -682,36 +822,33 @@ __device__ __forceinline__ bool await_partial(const LaunchArgs &args, uint32_t e
         ready = ok;
     }
     __syncthreads();
-    const bool ok = ready != 0;
+    // uniform by construction; readfirstlane tells the compiler so, which
+    // keeps everything derived from it (the next segment's bounds) scalar
+    const bool ok = __builtin_amdgcn_readfirstlane(ready) != 0;
     __syncthreads();               // `ready` is read by everyone before the next reuse
     return ok;
 }
 
 template <int NRB>
-__device__ __forceinline__ void add_partial(const LaunchArgs &args, int slot, int wave, f32x16 (&outer)[NRB][2])
+__device__ __forceinline__ void add_partial(const LaunchArgs &args, int slot, int wave, f32x4 (&outer)[NRB][2])
 {
     const int lane = lane_id();
     const __amdgpu_buffer_rsrc_t rs = partial_rsrc(args);
     const int base = partial_base(slot, wave);
-    // all loads of a row block first, then the adds: one memory latency per
-    // row block instead of one per load
+    // all loads first (the accumulators of the hot loop are dead here, so
+    // the registers exist), then the adds: one memory latency, not 2 NRB
+    f32x4 v[NRB][2];
 #pragma unroll
-    for (int i = 0; i < NRB; ++i) {
-        f32x4 v[2][4];
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                v[cb][q] = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16, base + ((i * 2 + cb) * 4 + q) * 1024,
-                                                                 kCoherent);
+    for (int i = 0; i < NRB; ++i)
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
+            v[i][cb] = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16, base + (i * 2 + cb) * 1024, kCoherent);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
+    for (int i = 0; i < NRB; ++i)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    outer[i][cb][4 * q + e] += v[cb][q][e];
-    }
+        for (int cb = 0; cb < 2; ++cb)
+            outer[i][cb] += v[i][cb];
 }
 
 // ---- accuracy fix-up ------------------------------------------------------
@@ -807,15 +944,16 @@ __device__ __noinline__ double exact_entry(const uint8_t *a, const uint8_t *sfa,
 }
 
 // The check and the exact recomputation for one finished tile (see above);
-// `parts` is the number of partial sums the finalizer added.
+// `parts` is the number of partial sums the finalizer added.  Lane (r, q)
+// holds outer[i][cb][e] = C[m0 + 16 i + 4 q + e][n0 + 32 wave + 16 cb + r].
 template <int NRB>
 __device__ __forceinline__ void fix_small_outputs(const GroupArgs &G, int m0, int rows, int n0, int wave, int parts,
-                                                  f32x16 (&outer)[NRB][2])
+                                                  f32x4 (&outer)[NRB][2])
 {
     const int lane = lane_id();
-    const int r = lane & 31, h = lane >> 5;
+    const int r = lane & 15, q = lane >> 4;
     const int row_end = m0 + rows;
-    const int col_base = n0 + kWaveCols * wave + r;
+    const int col_base = n0 + 32 * wave + r;
     float ss = 0.0f;
     int cnt = 0;
 #pragma unroll
@@ -823,10 +961,10 @@ __device__ __forceinline__ void fix_small_outputs(const GroupArgs &G, int m0, in
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int row = m0 + kBlockM * i + 8 * (v >> 2) + 4 * h + (v & 3);
-                const float x = outer[i][cb][v];
-                const bool use = row < row_end && col_base + 32 * cb < G.n && __builtin_isfinite(x);
+            for (int e = 0; e < 4; ++e) {
+                const int row = m0 + 16 * i + 4 * q + e;
+                const float x = outer[i][cb][e];
+                const bool use = row < row_end && col_base + 16 * cb < G.n && __builtin_isfinite(x);
                 ss += use ? x * x : 0.0f;
                 cnt += use ? 1 : 0;
             }
@@ -849,57 +987,57 @@ __device__ __forceinline__ void fix_small_outputs(const GroupArgs &G, int m0, in
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int row = m0 + kBlockM * i + 8 * (v >> 2) + 4 * h + (v & 3);
-                const int col = col_base + 32 * cb;
-                const bool flag = row < row_end && col < G.n && __builtin_fabsf(outer[i][cb][v]) < thresh;
+            for (int e = 0; e < 4; ++e) {
+                const int row = m0 + 16 * i + 4 * q + e;
+                const int col = col_base + 16 * cb;
+                const bool flag = row < row_end && col < G.n && __builtin_fabsf(outer[i][cb][e]) < thresh;
                 uint64_t todo = __ballot(flag);
                 while (todo) {
                     const int owner = __builtin_ctzll(todo);
                     todo &= todo - 1;
                     const int orow = __shfl(row, owner), ocol = __shfl(col, owner);
-                    const double e = exact_entry(G.a, G.sfa, G.b, G.sfb, orow, ocol, G.k);
+                    const double x = exact_entry(G.a, G.sfa, G.b, G.sfb, orow, ocol, G.k);
                     if (lane == owner)
-                        outer[i][cb][v] = (float)e;
+                        outer[i][cb][e] = (float)x;
                 }
             }
 }
 
-// One tile's share of this workgroup: units [ub, ue).  `w` is the logical
-// workgroup index.
-template <int NRB>
-__device__ __forceinline__ void run_tile(const LaunchArgs &args, uint32_t epoch, const TilePos &p, int ub, int ue,
-                                         int w, int wave, uint8_t *smem)
+// One tile's share of this workgroup: pairs [pb, pe).  `w` is the logical
+// workgroup index, [lo, hi) its cost range.
+template <int NRB, int W>
+__device__ __forceinline__ void run_tile(const LaunchArgs &args, uint32_t epoch, const TilePos &p, int pb, int pe, int w,
+                                         int wave, uint8_t *smem)
 {
     const GroupArgs &G = args.g[p.g];
     const int m0 = p.rt * G.tile_rows, n0 = p.strip * kTileN;
     const int rows = min(G.tile_rows, G.m - m0);
-    f32x16 outer[NRB][2];
+    f32x4 outer[NRB][2];
 #pragma unroll
     for (int i = 0; i < NRB; ++i)
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
-            outer[i][cb] = f32x16{};
+            outer[i][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
     // One call site of the pipelined loop: the own segment first, then (on
     // the finalizer) any producer part that did not arrive in time.
-    int sb = ub, se = ue, w2 = w;
+    int sb = pb, se = pe, w2 = w;
     int parts = 0;                 // partial sums added by this finalizer
     for (;;) {
-        segment<NRB>(G, m0, n0, wave, smem, sb, se, outer);
-        if (ub > 0) {              // a later part of a split tile
+        segment<NRB, W>(G, m0, n0, wave, smem, sb, se, outer);
+        if (pb > 0) {              // a later part of a split tile
             publish_partial<NRB>(args, epoch, w, wave, outer);
             return;
         }
         // finalizer: add the other parts of the tile in k order
         bool recompute = false;
-        const int64_t tile_end = p.cost_begin + kCostHead + (int64_t)G.nunits * p.ucost;
-        while (ue < G.nunits && ++w2 < args.num_wg) {
+        const int64_t tile_end = p.cost_begin + kCostHead + (int64_t)G.npairs * p.pcost;
+        while (pe < G.npairs && ++w2 < args.num_wg) {
             const int64_t lo = args.cut[w2];
             const int64_t hi = args.cut[w2 + 1];
             if (lo >= tile_end)
                 break;
             int qb, qe;
-            units_in(p, G.nunits, lo, hi, qb, qe);
+            pairs_in(p, G.npairs, lo, hi, qb, qe);
             if (qb >= qe)
                 continue;
             if (await_partial(args, epoch, w2)) {
@@ -920,7 +1058,8 @@ __device__ __forceinline__ void run_tile(const LaunchArgs &args, uint32_t epoch,
     store_tile<NRB>(G, m0, rows, n0, wave, outer);
 }
 
-__global__ __launch_bounds__(kThreads, 1) void nvfp4_group_gemm_kernel(const LaunchArgs args)
+template <int W>
+__global__ __launch_bounds__(64 * W, 1) void nvfp4_group_gemm_kernel(const LaunchArgs args)
 {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
 
@@ -939,18 +1078,22 @@ __global__ __launch_bounds__(kThreads, 1) void nvfp4_group_gemm_kernel(const Lau
 
     TilePos p = unpack_start(args, args.start[w]);
     while (p.g < args.ng) {
-        const int nunits = args.g[p.g].nunits;
-        int ub, ue;
-        units_in(p, nunits, lo, hi, ub, ue);
-        if (ub >= ue)
+        const int npairs = args.g[p.g].npairs;
+        int pb, pe;
+        pairs_in(p, npairs, lo, hi, pb, pe);
+        if (pb >= pe)
             break;
         switch (p.nrb) {
-        case 1: run_tile<1>(args, epoch, p, ub, ue, w, wave, smem); break;
-        case 2: run_tile<2>(args, epoch, p, ub, ue, w, wave, smem); break;
-        case 3: run_tile<3>(args, epoch, p, ub, ue, w, wave, smem); break;
-        default: run_tile<4>(args, epoch, p, ub, ue, w, wave, smem); break;
+        case 1: run_tile<1, W>(args, epoch, p, pb, pe, w, wave, smem); break;
+        case 2: run_tile<2, W>(args, epoch, p, pb, pe, w, wave, smem); break;
+        case 3: run_tile<3, W>(args, epoch, p, pb, pe, w, wave, smem); break;
+        case 4: run_tile<4, W>(args, epoch, p, pb, pe, w, wave, smem); break;
+        case 5: run_tile<5, W>(args, epoch, p, pb, pe, w, wave, smem); break;
+        case 6: run_tile<6, W>(args, epoch, p, pb, pe, w, wave, smem); break;
+        case 7: run_tile<7, W>(args, epoch, p, pb, pe, w, wave, smem); break;
+        default: run_tile<8, W>(args, epoch, p, pb, pe, w, wave, smem); break;
         }
-        if (ue < nunits)
+        if (pe < npairs)
             break;                 // the range ends inside this tile
         p = next_tile(args.g, args.ng, args.total_cost, p);
     }
@@ -1006,8 +1149,8 @@ int validate(const nvfp4_group_t *groups, int ng)
         const nvfp4_group_t &G = groups[i];
         if (G.m == 0 || G.n == 0)
             continue;
-        if (G.k % kStageK != 0)
-            return fail(NVFP4_EUNSUPPORTED, "group %d: k=%d is not a multiple of %d", i, G.k, kStageK);
+        if (G.k % 64 != 0)
+            return fail(NVFP4_EUNSUPPORTED, "group %d: k=%d is not a multiple of 64", i, G.k);
         if ((uint64_t)(G.m > G.n ? G.m : G.n) * (uint64_t)(G.k / 2) >= (1ull << 31))
             return fail(NVFP4_EUNSUPPORTED, "group %d: an operand reaches 2 GiB", i);
         if (((uintptr_t)G.c & 3u) != 0)
@@ -1022,11 +1165,11 @@ int validate(const nvfp4_group_t *groups, int ng)
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // Row tiling of a group: the fewest tiles of at most kTileM rows, with the
-// rows spread evenly (rounded up to 32) so a ragged M wastes little.
+// rows spread evenly (rounded up to 16) so a ragged M wastes little.
 inline void row_tiling(int m, int &tiles, int &rows_per_tile)
 {
     tiles = ceil_div(m, kTileM);
-    rows_per_tile = kBlockM * ceil_div(ceil_div(m, tiles), kBlockM);
+    rows_per_tile = 16 * ceil_div(ceil_div(m, tiles), 16);
     tiles = ceil_div(m, rows_per_tile);
 }
 
@@ -1053,13 +1196,13 @@ int pack_launch(const nvfp4_group_t *groups, int ng, int &next, LaunchArgs &args
         A.k = G.k;
         row_tiling(G.m, A.row_tiles, A.tile_rows);
         A.col_tiles = ceil_div(G.n, kTileN);
-        A.nunits = ceil_div(G.k, kUnitK);
-        if (A.nunits < 1)
-            A.nunits = 1;      // k == 0: one empty unit, the tile is still written
-        A.cost_full = unit_cost(A.tile_rows / kBlockM, A.nunits);
-        A.cost_last = unit_cost(tile_nrb(A, A.row_tiles - 1), A.nunits);
+        A.npairs = ceil_div(ceil_div(G.k, kStageK), 2);
+        if (A.npairs < 1)
+            A.npairs = 1;      // k == 0: one empty pair, the tile is still written
+        A.cost_full = pair_cost(A.tile_rows / 16, A.npairs);
+        A.cost_last = pair_cost(tile_nrb(A, A.row_tiles - 1), A.npairs);
         A.strip_cost = (int64_t)A.row_tiles * kCostHead +
-                       (int64_t)A.nunits * ((int64_t)(A.row_tiles - 1) * A.cost_full + A.cost_last);
+                       (int64_t)A.npairs * ((int64_t)(A.row_tiles - 1) * A.cost_full + A.cost_last);
         A.cost_begin = cost;
         args.group_begin[n - 1] = cost;
         cost += A.strip_cost * A.col_tiles;
@@ -1071,30 +1214,31 @@ int pack_launch(const nvfp4_group_t *groups, int ng, int &next, LaunchArgs &args
     return n;
 }
 
-int64_t total_units(const LaunchArgs &args)
+int64_t total_pairs(const LaunchArgs &args)
 {
     int64_t t = 0;
     for (int i = 0; i < args.ng; ++i)
-        t += (int64_t)args.g[i].row_tiles * args.g[i].col_tiles * args.g[i].nunits;
+        t += (int64_t)args.g[i].row_tiles * args.g[i].col_tiles * args.g[i].npairs;
     return t;
 }
 
 int grid_for(const LaunchArgs &args, int units)
 {
-    const int64_t tu = total_units(args);
-    int64_t g = tu < units ? tu : units;
+    const int64_t tp = total_pairs(args);
+    int64_t g = tp < units ? tp : units;
     if (g > kMaxWorkgroups)
         g = kMaxWorkgroups;
     return (int)g;
 }
 
-// Partition of a launch's (tile, unit) sequence among num_wg workgroups.
+// Partition of a launch's (tile, pair) sequence among num_wg workgroups.
 // A greedy fill against a target makespan, binary-searched: each workgroup
-// takes units in order while its modelled time stays within the target.
-// The model (clocks) charges a workgroup its start-up, a pipeline fill per
-// segment (the first one dearer), the units (per tile height: a unit of a
-// short tile is bound by streaming B, not by its MFMAs), and each
-// segment's epilogue:
+// takes pairs in order while its modelled time stays within the target.
+// The model (clocks, fitted to per-workgroup timestamps of this kernel on
+// MI355X) charges a workgroup its start-up, a pipeline fill per segment (the
+// first one dearer), the pairs (measured per tile height: a pair of a short
+// tile is bound by streaming B, not by its MFMAs), and each segment's
+// epilogue:
 //  * a whole tile: its store;
 //  * the later part of a split tile (its workgroup's first segment): the
 //    publish of its partial sums;
@@ -1107,20 +1251,30 @@ int grid_for(const LaunchArgs &args, int units)
 //    time for one sum and the store (the finalizer ends after the last part
 //    arrives, so a last part that ends at the makespan would set the
 //    makespan one sum and a store later).
-constexpr double kClkStart = 3000;
-constexpr double kClkFillFirst = 6000;
-constexpr double kClkFillNext = 4000;
-constexpr double kClkUnit[kRowBlocks + 1] = {0, 2800, 3300, 4200, 5200};
-constexpr double kClkPublish = 4000;
-constexpr double kClkStore = 3000;
-constexpr double kClkAdd = 3500;
+// Start-up, fills, store and publish are a least-squares fit of per-
+// workgroup timestamps (segment entry, loop start and end, kernel entry and
+// exit) over seven workloads; start-up and the first fill include the
+// workgroup's end-of-kernel work.  The pair costs, measured per tile height
+// on the balanced schedule, sit 6-14% above the bare loop's cost: they also
+// carry what a segment of short tiles pays beyond its loop, and a table
+// fitted to the loop alone balanced the ragged workloads worse.  The cost of
+// a finalizer's sum of one part (6000) is the value interleaved timing
+// preferred over 4000 and 8000: finalizers end 15-19k clk after their
+// tile's last part, more than one sum and a store at the fitted costs.
+constexpr double kClkStart = 3500;
+constexpr double kClkFillFirst = 5850;
+constexpr double kClkFillNext = 9400;
+constexpr double kClkPair[kRowBlocks + 1] = {0, 4212, 4634, 4648, 4880, 5305, 5622, 6141, 6988};
+constexpr double kClkPublish = 7900;
+constexpr double kClkStore = 7200;
+constexpr double kClkAdd = 6000;
 
 // One tile of the launch for the partition: where it starts in cost order,
-// its unit cost there, and its units' modelled clocks.
+// its pair cost there, and its pairs' modelled clocks.
 struct PlanTile {
     int64_t cost_begin;
-    int32_t ucost, nunits;
-    double unit_clk;
+    int32_t pcost, npairs;
+    double pair_clk;
 };
 
 bool greedy_cuts(const std::vector<PlanTile> &tiles, int nwg, int64_t total, double tmax, int64_t *cut)
@@ -1130,27 +1284,27 @@ bool greedy_cuts(const std::vector<PlanTile> &tiles, int nwg, int64_t total, dou
     bool fresh = true;             // workgroup w has no segment yet
     cut[0] = 0;
     for (const PlanTile &t : tiles) {
-        const int nunits = t.nunits;
-        const double uc = t.unit_clk;
+        const int npairs = t.npairs;
+        const double pc = t.pair_clk;
         int j = 0;
-        while (j < nunits) {
+        while (j < npairs) {
             const double base = cur + (fresh ? kClkFillFirst : kClkFillNext);
-            const int rest = nunits - j;
+            const int rest = npairs - j;
             const double epi_full = j == 0 ? kClkStore : kClkPublish;
             // a last part of a split tile leaves the finalizer its sum and store
             const double tail = j == 0 ? 0.0 : kClkAdd + kClkStore;
-            if (base + rest * uc + epi_full + tail <= tmax) {   // the rest of the tile fits
-                cur = base + rest * uc + epi_full;
+            if (base + rest * pc + epi_full + tail <= tmax) {   // the rest of the tile fits
+                cur = base + rest * pc + epi_full;
                 fresh = false;
                 break;
             }
-            // units this workgroup can take before its range ends in the tile
+            // pairs this workgroup can take before its range ends in the tile
             auto take = [&](double epi) {
-                const double fit = (tmax - base - epi) / uc;
+                const double fit = (tmax - base - epi) / pc;
                 return fit < 0 ? 0 : (fit > rest - 1 ? rest - 1 : (int)fit);
             };
-            auto next_takes_rest = [&](int rr) {
-                return kClkStart + kClkFillFirst + rr * uc + kClkPublish + kClkAdd + kClkStore <= tmax;
+            auto next_takes_rest = [&](int r) {
+                return kClkStart + kClkFillFirst + r * pc + kClkPublish + kClkAdd + kClkStore <= tmax;
             };
             int k;
             if (j == 0) {
@@ -1161,10 +1315,10 @@ bool greedy_cuts(const std::vector<PlanTile> &tiles, int nwg, int64_t total, dou
                 k = take(kClkPublish + kClkStore + 2 * kClkAdd);
             }
             j += k;
-            // workgroup w ends with unit j - 1 of this tile (or before the tile)
+            // workgroup w ends with pair j - 1 of this tile (or before the tile)
             if (++w >= nwg)
                 return false;
-            cut[w] = j == 0 ? t.cost_begin : t.cost_begin + kCostHead + (int64_t)j * t.ucost;
+            cut[w] = j == 0 ? t.cost_begin : t.cost_begin + kCostHead + (int64_t)j * t.pcost;
             cur = kClkStart;
             fresh = true;
         }
@@ -1198,9 +1352,9 @@ void plan_cuts(LaunchArgs &a, int nwg)
     std::vector<PlanTile> tiles;
     double work = 0, biggest = 0;
     for (TilePos p = locate(a, 0); p.g < a.ng; p = next_tile(a.g, a.ng, a.total_cost, p)) {
-        const PlanTile t{p.cost_begin, p.ucost, a.g[p.g].nunits, kClkUnit[p.nrb]};
-        const double tile = kClkFillFirst + kClkStore + 2 * kClkAdd + t.nunits * t.unit_clk;
-        work += t.nunits * t.unit_clk;
+        const PlanTile t{p.cost_begin, p.pcost, a.g[p.g].npairs, kClkPair[p.nrb]};
+        const double tile = kClkFillFirst + kClkStore + 2 * kClkAdd + t.npairs * t.pair_clk;
+        work += t.npairs * t.pair_clk;
         biggest = tile > biggest ? tile : biggest;
         tiles.push_back(t);
     }
@@ -1357,9 +1511,9 @@ extern "C" int nvfp4_plan(const nvfp4_group_t *groups, int ng, int num_workgroup
             TilePos p = unpack_start(args, args.start[w]);
             while (p.g < args.ng) {
                 const GroupArgs &G = args.g[p.g];
-                int ub, ue;
-                units_in(p, G.nunits, lo, hi, ub, ue);
-                if (ub >= ue)
+                int pb, pe;
+                pairs_in(p, G.npairs, lo, hi, pb, pe);
+                if (pb >= pe)
                     break;
                 if (segs != nullptr && count < cap) {
                     int32_t *o = segs + 8 * count;
@@ -1369,12 +1523,12 @@ extern "C" int nvfp4_plan(const nvfp4_group_t *groups, int ng, int num_workgroup
                     o[2] = m0;
                     o[3] = G.m - m0 < G.tile_rows ? G.m - m0 : G.tile_rows;
                     o[4] = p.strip * kTileN;
-                    o[5] = kUnitK * ub;
-                    o[6] = kUnitK * ue;
-                    o[7] = (ub == 0 && ue == G.nunits) ? 0 : (ub > 0 ? 1 : 2);
+                    o[5] = 2 * kStageK * pb;
+                    o[6] = 2 * kStageK * pe;
+                    o[7] = (pb == 0 && pe == G.npairs) ? 0 : (pb > 0 ? 1 : 2);
                 }
                 ++count;
-                if (ue < G.nunits)
+                if (pe < G.npairs)
                     break;
                 p = next_tile(args.g, args.ng, args.total_cost, p);
             }
@@ -1415,7 +1569,7 @@ extern "C" int nvfp4_group_gemm(const nvfp4_group_t *groups, int ng, void *strea
         args.flags = ws->flags;
         args.control = ws->flags + ws->slots;
         args.spin_limit = spin_limit();
-        hipLaunchKernelGGL(nvfp4_group_gemm_kernel, dim3((unsigned)nwg), dim3(kThreads), 0, st, args);
+        hipLaunchKernelGGL((nvfp4_group_gemm_kernel<kWaves>), dim3((unsigned)nwg), dim3(kThreads), 0, st, args);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return fail(NVFP4_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
