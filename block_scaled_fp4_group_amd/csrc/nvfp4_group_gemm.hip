@@ -867,85 +867,109 @@ __device__ __forceinline__ void add_partial(const LaunchArgs &args, int slot, in
 // folds and part sums).  Outputs with 2e-3 |c| + 1e-2 < kSigmaMargin *
 // sigma are recomputed exactly.  Calibrated on the hardware's rounding
 // model over the five benchmark workloads, the largest error of an output
-// small next to rms(C) is 3.3 sigma.
-constexpr float kSigmaMargin = 6.0f;
+// small next to rms(C) is 3.3 sigma (the rms error is about 0.25 sigma).
+constexpr float kSigmaMargin = 5.0f;
 constexpr float kTolRel = 2e-3f;
 constexpr float kTolAbs = 1e-2f;
 
-// Sum of the products of eight E2M1 code pairs (one dword each), exact in
-// fp32 (multiples of 1/4 below 2^9).
-__device__ __forceinline__ float code_dot8(uint32_t xa, uint32_t xb)
+// Exact sum of the products of eight E2M1 code pairs (one dword each): the
+// codes are converted to fp16 (exact) and multiplied and summed in fp32 by
+// packed dot products; every partial sum is a multiple of 1/4 below 2^9, so
+// nothing rounds.
+__device__ __forceinline__ float code_dot8_f16(uint32_t xa, uint32_t xb, float acc)
 {
-    float s = 0.0f;
-    const auto a0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(xa, 1.0f, 0);
-    const auto b0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(xb, 1.0f, 0);
-    const auto a1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(xa, 1.0f, 1);
-    const auto b1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(xb, 1.0f, 1);
-    const auto a2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(xa, 1.0f, 2);
-    const auto b2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(xb, 1.0f, 2);
-    const auto a3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(xa, 1.0f, 3);
-    const auto b3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(xb, 1.0f, 3);
-    s += a0[0] * b0[0];
-    s += a0[1] * b0[1];
-    s += a1[0] * b1[0];
-    s += a1[1] * b1[1];
-    s += a2[0] * b2[0];
-    s += a2[1] * b2[1];
-    s += a3[0] * b3[0];
-    s += a3[1] * b3[1];
-    return s;
+    acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(xa, 1.0f, 0),
+                                 __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(xb, 1.0f, 0), acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(xa, 1.0f, 1),
+                                 __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(xb, 1.0f, 1), acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(xa, 1.0f, 2),
+                                 __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(xb, 1.0f, 2), acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(xa, 1.0f, 3),
+                                 __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(xb, 1.0f, 3), acc, false);
+    return acc;
 }
 
-// Exact value of one output: per 16-k block, the sum of the 16 code
-// products is exact in fp32 (multiples of 1/4, |sum| <= 576), times both
-// block scales exact in fp64, summed over blocks in fp64.  Every lane takes
-// blocks lane, lane + 64, ...; the wave's partial sums are combined at the
-// end, and every lane returns the total.
-__device__ __noinline__ double exact_entry(const uint8_t *a, const uint8_t *sfa, const uint8_t *b, const uint8_t *sfb,
-                                           int m, int n, int K)
+// Exact values of two outputs (rows m[j], columns n[j] of one group; a
+// repeated pair is fine).  Per 16-k block the sum of the 16 code products is
+// exact in fp32 (multiples of 1/4, |sum| <= 576), and so is its product with
+// both block scales (at most 20 significant bits); the blocks are summed in
+// fp64.  Lane l takes blocks 4 l .. 4 l + 3 of every 256-block pass, so a
+// pass issues every load of both outputs before waiting for any (one pass
+// for K <= 4096); the wave's partial sums are combined at the end and every
+// lane returns the totals.
+struct Exact2 {
+    double v[2];
+};
+
+__device__ __forceinline__ Exact2 exact2(const uint8_t *a, const uint8_t *sfa, const uint8_t *b, const uint8_t *sfb,
+                                         int M, int N, int K, int m0, int n0, int m1, int n1)
 {
     const int lane = threadIdx.x & 63;
     const int nb = K >> 4;
-    const uint8_t *ar = a + (size_t)m * (size_t)(K >> 1);
-    const uint8_t *br = b + (size_t)n * (size_t)(K >> 1);
-    const uint8_t *sar = sfa + (size_t)m * (size_t)nb;
-    const uint8_t *sbr = sfb + (size_t)n * (size_t)nb;
-    double acc = 0.0;
-    for (int blk0 = 0; blk0 < nb; blk0 += 64 * 8) {
-        uint2 ca[8], cb[8];
-        uint32_t sa[8], sb[8];
-        // all loads of up to eight blocks first: one memory latency
+    const uint32_t row_bytes = (uint32_t)K >> 1, row_sc = (uint32_t)K >> 4;
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void *)a, 0, M * (int)row_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void *)b, 0, N * (int)row_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc((void *)sfa, 0, M * (int)row_sc, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc((void *)sfb, 0, N * (int)row_sc, 0x00020000);
+    const int mm[2] = {m0, m1}, nn[2] = {n0, n1};
+    double acc[2] = {0.0, 0.0};
+    for (int base = 0; base < nb; base += 256) {
+        const int blk = base + 4 * lane;   // nb % 4 == 0: a lane's four blocks are all in or all out
+        const bool in = blk < nb;
+        u32x4 ca[2][2], cb[2][2];
+        uint32_t sa[2], sb[2];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int blk = blk0 + 64 * j + lane;
-            const bool in = blk < nb;
-            ca[j] = in ? *reinterpret_cast<const uint2 *>(ar + 8 * blk) : make_uint2(0, 0);
-            cb[j] = in ? *reinterpret_cast<const uint2 *>(br + 8 * blk) : make_uint2(0, 0);
-            sa[j] = in ? sar[blk] : 0u;
-            sb[j] = in ? sbr[blk] : 0u;
+        for (int j = 0; j < 2; ++j) {
+            const uint32_t oa = (uint32_t)mm[j] * row_bytes + 8u * (uint32_t)blk;
+            const uint32_t ob = (uint32_t)nn[j] * row_bytes + 8u * (uint32_t)blk;
+            ca[j][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, oa, 0, 0));
+            ca[j][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, oa + 16u, 0, 0));
+            cb[j][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, ob, 0, 0));
+            cb[j][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, ob + 16u, 0, 0));
+            sa[j] = __builtin_amdgcn_raw_buffer_load_b32(rsa, (uint32_t)mm[j] * row_sc + (uint32_t)blk, 0, 0);
+            sb[j] = __builtin_amdgcn_raw_buffer_load_b32(rsb, (uint32_t)nn[j] * row_sc + (uint32_t)blk, 0, 0);
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            float s = 0.0f;
+        for (int j = 0; j < 2; ++j) {
+            float prod[4];
 #pragma unroll
-            for (int w = 0; w < 2; ++w) {
-                const uint32_t xa = w ? ca[j].y : ca[j].x, xb = w ? cb[j].y : cb[j].x;
-                s += code_dot8(xa, xb);
+            for (int t = 0; t < 4; ++t) {
+                const u32x4 &xa = ca[j][t >> 1], &xb = cb[j][t >> 1];
+                const int d = 2 * (t & 1);
+                prod[t] = code_dot8_f16(xa[d + 1], xb[d + 1], code_dot8_f16(xa[d], xb[d], 0.0f));
             }
-            const double scale = (double)__builtin_amdgcn_cvt_scalef32_f32_fp8(sa[j], 1.0f, 0) *
-                                 (double)__builtin_amdgcn_cvt_scalef32_f32_fp8(sb[j], 1.0f, 0);
-            acc += (double)s * scale;
+            const float s0 = __builtin_amdgcn_cvt_scalef32_f32_fp8(sa[j], 1.0f, 0) *
+                             __builtin_amdgcn_cvt_scalef32_f32_fp8(sb[j], 1.0f, 0);
+            const float s1 = __builtin_amdgcn_cvt_scalef32_f32_fp8(sa[j], 1.0f, 1) *
+                             __builtin_amdgcn_cvt_scalef32_f32_fp8(sb[j], 1.0f, 1);
+            const float s2 = __builtin_amdgcn_cvt_scalef32_f32_fp8(sa[j], 1.0f, 2) *
+                             __builtin_amdgcn_cvt_scalef32_f32_fp8(sb[j], 1.0f, 2);
+            const float s3 = __builtin_amdgcn_cvt_scalef32_f32_fp8(sa[j], 1.0f, 3) *
+                             __builtin_amdgcn_cvt_scalef32_f32_fp8(sb[j], 1.0f, 3);
+            const double part = (double)(prod[0] * s0) + (double)(prod[1] * s1) + (double)(prod[2] * s2) +
+                                (double)(prod[3] * s3);
+            acc[j] += in ? part : 0.0;
         }
     }
+    Exact2 r;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        acc += __shfl_xor(acc, off);
-    return acc;
+    for (int j = 0; j < 2; ++j) {
+        double x = acc[j];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1)
+            x += __shfl_xor(x, off);
+        r.v[j] = x;
+    }
+    return r;
 }
 
 // The check and the exact recomputation for one finished tile (see above);
 // `parts` is the number of partial sums the finalizer added.  Lane (r, q)
 // holds outer[i][cb][e] = C[m0 + 16 i + 4 q + e][n0 + 32 wave + 16 cb + r].
+// The outputs at risk are visited twice in the same order: the first pass
+// lists them (position p of the list in lane p) and their exact values are
+// computed two at a time; the second pass writes each back to its lane.
+// More than 64 at risk take further rounds.
 template <int NRB>
 __device__ __forceinline__ void fix_small_outputs(const GroupArgs &G, int m0, int rows, int n0, int wave, int parts,
                                                   f32x4 (&outer)[NRB][2])
@@ -954,53 +978,99 @@ __device__ __forceinline__ void fix_small_outputs(const GroupArgs &G, int m0, in
     const int r = lane & 15, q = lane >> 4;
     const int row_end = m0 + rows;
     const int col_base = n0 + 32 * wave + r;
+    // rms over every sum the wave holds: rows and columns past the group
+    // repeat its last row or column (the operand loads are clamped), which
+    // leaves the estimate unbiased enough for a threshold
     float ss = 0.0f;
-    int cnt = 0;
 #pragma unroll
     for (int i = 0; i < NRB; ++i)
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = m0 + 16 * i + 4 * q + e;
-                const float x = outer[i][cb][e];
-                const bool use = row < row_end && col_base + 16 * cb < G.n && __builtin_isfinite(x);
-                ss += use ? x * x : 0.0f;
-                cnt += use ? 1 : 0;
-            }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        ss += __shfl_xor(ss, off);
-        cnt += __shfl_xor(cnt, off);
+            for (int e = 0; e < 4; ++e)
+                ss = __builtin_fmaf(outer[i][cb][e], outer[i][cb][e], ss);
+    // inclusive scan within each row of 16 lanes, then the four row totals
+    ss += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, ss), 0x111, 0xF, 0xF, true));
+    ss += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, ss), 0x112, 0xF, 0xF, true));
+    ss += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, ss), 0x114, 0xF, 0xF, true));
+    ss += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, ss), 0x118, 0xF, 0xF, true));
+    {
+        const int si = __builtin_bit_cast(int, ss);
+        ss = __builtin_bit_cast(float, __builtin_amdgcn_readlane(si, 15)) +
+             __builtin_bit_cast(float, __builtin_amdgcn_readlane(si, 31)) +
+             __builtin_bit_cast(float, __builtin_amdgcn_readlane(si, 47)) +
+             __builtin_bit_cast(float, __builtin_amdgcn_readlane(si, 63));
     }
-    if (cnt == 0)
-        return;
+    const float cnt = (float)(NRB * 8 * 64);
+    if (!__builtin_isfinite(ss))
+        ss = 0x1p100f;             // a non-finite sum: every output of the wave is checked exactly
     const float K = (float)G.k;
     const float F = (float)(kFoldStages * kStageK);
-    const float sigma = 0x1p-24f * __builtin_sqrtf(ss / (float)cnt) *
+    const float sigma = 0x1p-24f * __builtin_sqrtf(ss / cnt) *
                         __builtin_sqrtf(fminf(F, K) / 16.0f + K / (2.0f * F) + (float)parts);
     const float thresh = (kSigmaMargin * sigma - kTolAbs) / kTolRel;   // recompute |c| < thresh
     if (!(thresh > 0.0f))
         return;
+    auto at_risk = [&](int i, int cb, int e) {
+        const int row = m0 + 16 * i + 4 * q + e;
+        return row < row_end && col_base + 16 * cb < G.n && __builtin_fabsf(outer[i][cb][e]) < thresh;
+    };
+    for (int round = 0;; ++round) {
+        // pass 1: list entries [64 round, 64 round + 64) in lanes 0..63
+        int lrow = 0, lcol = 0, n = 0, seen = 0;
 #pragma unroll
-    for (int i = 0; i < NRB; ++i)
+        for (int i = 0; i < NRB; ++i)
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
+            for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = m0 + 16 * i + 4 * q + e;
-                const int col = col_base + 16 * cb;
-                const bool flag = row < row_end && col < G.n && __builtin_fabsf(outer[i][cb][e]) < thresh;
-                uint64_t todo = __ballot(flag);
-                while (todo) {
-                    const int owner = __builtin_ctzll(todo);
-                    todo &= todo - 1;
-                    const int orow = __shfl(row, owner), ocol = __shfl(col, owner);
-                    const double x = exact_entry(G.a, G.sfa, G.b, G.sfb, orow, ocol, G.k);
-                    if (lane == owner)
-                        outer[i][cb][e] = (float)x;
+                for (int e = 0; e < 4; ++e) {
+                    uint64_t todo = __ballot(at_risk(i, cb, e));
+                    while (todo) {
+                        const int owner = __builtin_ctzll(todo);
+                        todo &= todo - 1;
+                        if (seen >= 64 * round && n < 64) {
+                            const int orow = m0 + 16 * i + 4 * (owner >> 4) + e;
+                            const int ocol = n0 + 32 * wave + 16 * cb + (owner & 15);
+                            lrow = lane == n ? orow : lrow;
+                            lcol = lane == n ? ocol : lcol;
+                            ++n;
+                        }
+                        ++seen;
+                    }
                 }
-            }
+        if (n == 0)
+            return;
+        // exact values, two at a time (a short last batch repeats its entry)
+        double lval = 0.0;
+        for (int p = 0; p < n; p += 2) {
+            const int p1 = p + 1 < n ? p + 1 : p;
+            const Exact2 x = exact2(G.a, G.sfa, G.b, G.sfb, G.m, G.n, G.k, __builtin_amdgcn_readlane(lrow, p),
+                                    __builtin_amdgcn_readlane(lcol, p), __builtin_amdgcn_readlane(lrow, p1),
+                                    __builtin_amdgcn_readlane(lcol, p1));
+            lval = lane == p ? x.v[0] : lval;
+            lval = lane == p1 ? x.v[1] : lval;
+        }
+        // pass 2: the same visit order; entry k goes back to its owner
+        int k = 0;
+#pragma unroll
+        for (int i = 0; i < NRB; ++i)
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const bool risk = at_risk(i, cb, e);
+                    uint64_t todo = __ballot(risk);
+                    // this lane's rank among the set lanes of this element
+                    const int below = __builtin_popcountll(todo & ((1ull << lane) - 1));
+                    const int idx = k + below - 64 * round;
+                    const double v = __shfl(lval, idx & 63);
+                    if (risk && idx >= 0 && idx < n)
+                        outer[i][cb][e] = (float)v;
+                    k += __builtin_popcountll(todo);
+                }
+        if (n < 64)
+            return;
+    }
 }
 
 // One tile's share of this workgroup: pairs [pb, pe).  `w` is the logical
