@@ -12,7 +12,8 @@ import os
 from typing import Iterable, List, Sequence, Tuple
 
 __all__ = ["NVFP4_OK", "NVFP4_EINVAL", "NVFP4_EUNSUPPORTED", "NVFP4_EHIP", "Nvfp4Error",
-           "Nvfp4Group", "lib", "library_path", "group_gemm", "group_gemm_raw", "validate",
+           "Nvfp4Group", "lib", "library_path", "group_gemm", "group_gemm_raw", "group_gemm_noalloc_raw",
+           "validate",
            "plan", "release_workspace", "tile_rows", "tile_cols", "make_group"]
 
 NVFP4_OK, NVFP4_EINVAL, NVFP4_EUNSUPPORTED, NVFP4_EHIP = 0, 1, 2, 3
@@ -46,6 +47,8 @@ def lib():
         gp = ctypes.POINTER(Nvfp4Group)
         L.nvfp4_group_gemm.restype = ctypes.c_int
         L.nvfp4_group_gemm.argtypes = [gp, ctypes.c_int, ctypes.c_void_p]
+        L.nvfp4_group_gemm_noalloc.restype = ctypes.c_int
+        L.nvfp4_group_gemm_noalloc.argtypes = [gp, ctypes.c_int, ctypes.c_void_p]
         L.nvfp4_validate.restype = ctypes.c_int
         L.nvfp4_validate.argtypes = [gp, ctypes.c_int]
         L.nvfp4_plan.restype = ctypes.c_int
@@ -77,6 +80,15 @@ def group_gemm_raw(groups: Sequence[Nvfp4Group], stream: int = 0) -> None:
     """Call nvfp4_group_gemm with prepared descriptors on a raw hipStream_t."""
     arr = _array(groups)
     rc = lib().nvfp4_group_gemm(arr, len(groups), ctypes.c_void_p(stream or None))
+    if rc != NVFP4_OK:
+        raise Nvfp4Error(rc, _last_error())
+
+
+def group_gemm_noalloc_raw(groups: Sequence[Nvfp4Group], stream: int = 0) -> None:
+    """Call nvfp4_group_gemm_noalloc (no device allocation: the library's
+    fixed per-GPU workspace; overlapping calls on one GPU race)."""
+    arr = _array(groups)
+    rc = lib().nvfp4_group_gemm_noalloc(arr, len(groups), ctypes.c_void_p(stream or None))
     if rc != NVFP4_OK:
         raise Nvfp4Error(rc, _last_error())
 

@@ -1543,6 +1543,88 @@ int device_units(int &device, int &units)
     return NVFP4_OK;
 }
 
+// Allocation-free variant: the same workspace layout (partial-sum slots,
+// their flags, two control words) in a file-scope device array instead of a
+// per-stream allocation.  Each GPU the library runs on holds its own copy
+// until the process ends; it starts zeroed (the loader clears it), which is
+// the state the epoch logic needs, so nothing is cleared per call.  Host code
+// reaches it only through the address hipGetSymbolAddress returns for the
+// current device (the array's name in host code is a stand-in, not a device
+// address).
+constexpr int kStaticSlots = kMaxWorkgroups;
+constexpr size_t kStaticPartialBytes = (size_t)kStaticSlots * kPartialSlot;
+constexpr size_t kStaticBytes = kStaticPartialBytes + ((size_t)kStaticSlots + 64) * sizeof(uint32_t);
+static __device__ __align__(256) uint8_t scratch[kStaticBytes];
+
+// Device address of `scratch` on the current device, looked up once per
+// device and kept.
+int static_scratch(int device, uint8_t *&out)
+{
+    static std::mutex m;
+    static std::map<int, uint8_t *> addr;
+    std::lock_guard<std::mutex> lock(m);
+    auto it = addr.find(device);
+    if (it == addr.end()) {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || ptr == nullptr)
+            return fail(NVFP4_EHIP, "cannot find the static workspace on device %d: %s", device,
+                        hipGetErrorString(e));
+        it = addr.emplace(device, static_cast<uint8_t *>(ptr)).first;
+    }
+    out = it->second;
+    return NVFP4_OK;
+}
+
+// Every launch of one call: the stream's allocated workspace, or (use_static)
+// the device's static one.
+int launch_all(const nvfp4_group_t *groups, int ng, hipStream_t st, bool use_static)
+{
+    int device = 0, units = 0;
+    LaunchArgs args;
+    int next = 0;
+    bool queried = false;
+    while (next < ng) {
+        if (pack_launch(groups, ng, next, args) == 0)
+            break;
+        if (!queried) {
+            const int rc2 = device_units(device, units);
+            if (rc2 != NVFP4_OK)
+                return rc2;
+            queried = true;
+        }
+        const int nwg = grid_for(args, units);
+        if (use_static) {
+            if (nwg > kStaticSlots)
+                return fail(NVFP4_EUNSUPPORTED, "%d workgroups exceed the static workspace's %d slots", nwg,
+                            kStaticSlots);
+            uint8_t *base = nullptr;
+            const int rc3 = static_scratch(device, base);
+            if (rc3 != NVFP4_OK)
+                return rc3;
+            args.partials = reinterpret_cast<float *>(base);
+            args.flags = reinterpret_cast<uint32_t *>(base + kStaticPartialBytes);
+            args.control = args.flags + kStaticSlots;
+        } else {
+            Workspace *ws = nullptr;
+            const int rc3 = workspace_for(st, device, units < kMaxWorkgroups ? units : kMaxWorkgroups, ws);
+            if (rc3 != NVFP4_OK)
+                return rc3;
+            args.partials = ws->partials;
+            args.flags = ws->flags;
+            args.control = ws->flags + ws->slots;
+        }
+        args.num_wg = nwg;
+        plan_cuts(args, nwg);
+        args.spin_limit = spin_limit();
+        hipLaunchKernelGGL((nvfp4_group_gemm_kernel<kWaves>), dim3((unsigned)nwg), dim3(kThreads), 0, st, args);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return fail(NVFP4_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+    }
+    return NVFP4_OK;
+}
+
 }  // namespace
 
 extern "C" int nvfp4_validate(const nvfp4_group_t *groups, int ng)
@@ -1614,37 +1696,15 @@ extern "C" int nvfp4_group_gemm(const nvfp4_group_t *groups, int ng, void *strea
     const int rc = validate(groups, ng);
     if (rc != NVFP4_OK)
         return rc;
-    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    int device = 0, units = 0;
-    LaunchArgs args;
-    int next = 0;
-    bool queried = false;
-    while (next < ng) {
-        if (pack_launch(groups, ng, next, args) == 0)
-            break;
-        if (!queried) {
-            const int rc2 = device_units(device, units);
-            if (rc2 != NVFP4_OK)
-                return rc2;
-            queried = true;
-        }
-        const int nwg = grid_for(args, units);
-        Workspace *ws = nullptr;
-        const int rc3 = workspace_for(st, device, units < kMaxWorkgroups ? units : kMaxWorkgroups, ws);
-        if (rc3 != NVFP4_OK)
-            return rc3;
-        args.num_wg = nwg;
-        plan_cuts(args, nwg);
-        args.partials = ws->partials;
-        args.flags = ws->flags;
-        args.control = ws->flags + ws->slots;
-        args.spin_limit = spin_limit();
-        hipLaunchKernelGGL((nvfp4_group_gemm_kernel<kWaves>), dim3((unsigned)nwg), dim3(kThreads), 0, st, args);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess)
-            return fail(NVFP4_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
-    }
-    return NVFP4_OK;
+    return launch_all(groups, ng, reinterpret_cast<hipStream_t>(stream), false);
+}
+
+extern "C" int nvfp4_group_gemm_noalloc(const nvfp4_group_t *groups, int ng, void *stream)
+{
+    const int rc = validate(groups, ng);
+    if (rc != NVFP4_OK)
+        return rc;
+    return launch_all(groups, ng, reinterpret_cast<hipStream_t>(stream), true);
 }
 
 extern "C" int nvfp4_release_workspace(void *stream)

@@ -102,6 +102,23 @@ typedef struct nvfp4_group {
 int nvfp4_group_gemm(const nvfp4_group_t *groups, int ng, void *stream);
 
 /*
+ * The same operation for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  It calls no hipMalloc, hipFree or other allocating routine.
+ * Instead of the per-stream workspace it uses one fixed device array of the
+ * library (32 MiB of partial-sum slots for up to 256 workgroups, plus 1.3
+ * KiB of flags and control words), which every GPU the library runs on
+ * holds from the library's load until the process ends.  Every call on a
+ * GPU shares that GPU's array: calls that overlap on one GPU (on any
+ * streams, including nvfp4_group_gemm_noalloc calls on two streams) race
+ * and must be ordered by the caller.  Arguments, errors, results and graph
+ * capture are as for nvfp4_group_gemm (a capturing stream needs no prior
+ * call); a launch that would need more workgroups than the array has slots
+ * returns NVFP4_EUNSUPPORTED (not on MI355X, whose 256 compute units all fit).
+ */
+int nvfp4_group_gemm_noalloc(const nvfp4_group_t *groups, int ng, void *stream);
+
+/*
  * Host-only argument check: the same validation nvfp4_group_gemm performs,
  * without touching the GPU.  Returns one of the codes above.
  */
