@@ -14,7 +14,7 @@ from typing import Iterable, List, Sequence, Tuple
 __all__ = ["NVFP4_OK", "NVFP4_EINVAL", "NVFP4_EUNSUPPORTED", "NVFP4_EHIP", "Nvfp4Error",
            "Nvfp4Group", "lib", "library_path", "group_gemm", "group_gemm_raw", "group_gemm_noalloc_raw",
            "validate",
-           "plan", "release_workspace", "tile_rows", "tile_cols", "make_group"]
+           "plan", "release_workspace", "stream_errors", "tile_rows", "tile_cols", "make_group"]
 
 NVFP4_OK, NVFP4_EINVAL, NVFP4_EUNSUPPORTED, NVFP4_EHIP = 0, 1, 2, 3
 
@@ -55,6 +55,8 @@ def lib():
         L.nvfp4_plan.argtypes = [gp, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int32), ctypes.c_int]
         L.nvfp4_release_workspace.restype = ctypes.c_int
         L.nvfp4_release_workspace.argtypes = [ctypes.c_void_p]
+        L.nvfp4_stream_errors.restype = ctypes.c_int
+        L.nvfp4_stream_errors.argtypes = [ctypes.c_void_p]
         L.nvfp4_tile_rows.restype = ctypes.c_int
         L.nvfp4_tile_cols.restype = ctypes.c_int
         L.nvfp4_last_error.restype = ctypes.c_char_p
@@ -119,6 +121,15 @@ def release_workspace(stream: int = 0) -> None:
     rc = lib().nvfp4_release_workspace(ctypes.c_void_p(stream or None))
     if rc != NVFP4_OK:
         raise Nvfp4Error(rc, _last_error())
+
+
+def stream_errors(stream: int = 0) -> int:
+    """Synchronise a raw hipStream_t and return (and clear) the count of
+    hand-off waits that ran out since the last check (0 when all is well)."""
+    rc = lib().nvfp4_stream_errors(ctypes.c_void_p(stream or None))
+    if rc < 0:
+        raise Nvfp4Error(-rc, _last_error())
+    return rc
 
 
 def tile_rows() -> int:

@@ -119,9 +119,12 @@ struct LaunchArgs {
     uint32_t *flags;     // num_wg flags: slot holds this launch's partial when == its epoch
     // [0]: epoch of the last finished launch on this workspace, [1]:
     // workgroups of this launch that have finished (device-resident, so a
-    // launch replayed from a captured graph still gets a fresh epoch)
+    // launch replayed from a captured graph still gets a fresh epoch), [2]:
+    // hand-off waits that ran out (a sticky count, read and cleared by
+    // nvfp4_stream_errors)
     uint32_t *control;
     int32_t spin_limit;  // flag polls before a missing part is recomputed instead
+    int32_t sync_spin_limit;  // polls of an A hand-off wait before it gives up (and counts an error)
     // Workgroup w's range is the cost interval (cut[w], cut[w + 1]]: the
     // pairs whose end cost lies in it belong to w (cut[0] = 0, cut[num_wg] =
     // total_cost, non-decreasing; chosen on the host)
@@ -260,6 +263,7 @@ __host__ __device__ inline void pairs_in(const TilePos &p, int npairs, int64_t l
 }
 
 // Bytes of one workgroup's partial-sum slot: [wave][row block][cb][lane] f32x4.
+constexpr int kControlWords = 4;
 constexpr uint32_t kPartialSlot = kWaves * kRowBlocks * 2u * 64u * 16u;
 
 // ---------------------------------------------------------------- device --
@@ -396,9 +400,10 @@ __device__ __forceinline__ int lane_id()
 // c + 1 from overtaking a slower wave's reads of stage c - 1.  LDS performs
 // a wave's operations in issue order, so a count is added only after the
 // wave's writes.  Waves thus drift up to a stage apart, and one wave's
-// decode overlaps another's MFMAs.  The wait is bounded (a broken count
-// gives wrong sums instead of a hang).
-constexpr int kSyncSpinLimit = 1 << 14;
+// decode overlaps another's MFMAs.  The wait is bounded: a count that never
+// arrives (which would be a bug) gives wrong sums instead of a hang, and is
+// recorded in a device error word the host can read (nvfp4_stream_errors).
+constexpr int kSyncSpinLimit = 1 << 14;   // default polls (NVFP4_SYNC_SPIN_LIMIT overrides)
 // Both are single asm statements so that the hot loop stays one basic
 // block for the compiler; the LDS operations they add only make the
 // compiler's own (in-order) LDS waits more conservative.
@@ -407,10 +412,11 @@ constexpr int kSyncSpinLimit = 1 << 14;
 // wait ends without a new read (whose lgkmcnt(0) would drain every LDS
 // operation in flight), and the compiler's wait for `pre` covers only the
 // LDS operations issued before it.
-__device__ __forceinline__ void half_wait(uint32_t count_addr, int target, int pre)
+// Polls at most `limit` + 1 times; returns true if the wait ran out.
+__device__ __forceinline__ bool half_wait(uint32_t count_addr, int target, int pre, int limit)
 {
     int v;
-    int seen, left = kSyncSpinLimit;
+    int seen, left = limit + 1;
     asm volatile("v_readfirstlane_b32 %1, %5\n\t"
                  "s_cmp_ge_i32 %1, %4\n\t"
                  "s_cbranch_scc1 2f\n"
@@ -428,6 +434,7 @@ __device__ __forceinline__ void half_wait(uint32_t count_addr, int target, int p
                  : "=&v"(v), "=&s"(seen), "+s"(left)
                  : "v"(count_addr), "s"(target), "v"(pre)
                  : "memory", "scc");
+    return left <= 0;
 }
 // Early read of a counter for half_wait (a volatile LDS load, so it stays
 // where it is issued relative to the other LDS operations).
@@ -453,7 +460,8 @@ __device__ __forceinline__ void half_done(uint32_t count_addr, uint32_t one)
 // tile is rows [m0, m0 + 16 NRB) and columns [n0, n0 + 32 W) of one group.
 // Lane (r, q) of wave w holds outer[i][cb][e] = C[m0 + 16i + 4q + e][n0 + 32w + 16cb + r].
 template <int NRB, int W>
-__device__ __forceinline__ void segment(const GroupArgs &G, int m0, int n0, int wave, uint8_t *smem,
+__device__ __forceinline__ void segment(const GroupArgs &G, uint32_t *err, int sync_limit, int m0, int n0, int wave,
+                                        uint8_t *smem,
                                         int pb, int pe, f32x4 (&outer)[NRB][2])
 {
     const int M = G.m, N = G.n, K = G.k;
@@ -499,6 +507,7 @@ __device__ __forceinline__ void segment(const GroupArgs &G, int m0, int n0, int 
     };
 
     f32x4 inner[NRB][2];
+    bool late = false;  // a hand-off wait ran out
     f16x8 bf[2][4];     // decoded B operands of the current stage, per MFMA step
     f16x8 af[NRB];
 
@@ -618,7 +627,7 @@ __device__ __forceinline__ void segment(const GroupArgs &G, int m0, int n0, int 
         }
         const u32x4 ac_next = a_codes(nslot);
         const int ready = __builtin_amdgcn_readfirstlane(kWaves * (c - c_begin));
-        half_wait(sync_addr, ready, pre0);
+        late |= half_wait(sync_addr, ready, pre0, sync_limit);
 #pragma unroll
         for (int i = 0; i < NRB; ++i)
             af[i] = aop(kBuf, i, 0);
@@ -629,7 +638,7 @@ __device__ __forceinline__ void segment(const GroupArgs &G, int m0, int n0, int 
         for (int s = 0; s < 4; ++s) {
             __builtin_amdgcn_sched_barrier(0);
             if (s == 1)
-                half_wait(sync_addr + 4u, ready, pre1);   // step 2's fragments are read during step 1
+                late |= half_wait(sync_addr + 4u, ready, pre1, sync_limit);   // step 2's fragments are read during step 1
 #pragma unroll
             for (int i = 0; i < NRB; ++i) {
 #pragma unroll
@@ -690,6 +699,8 @@ __device__ __forceinline__ void segment(const GroupArgs &G, int m0, int n0, int 
     }
     // drain the clamped prefetches before the LDS is reused
     wait_vmcnt<0>();
+    if (late && (threadIdx.x & 63) == 0)
+        __hip_atomic_fetch_add(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     }
 }
@@ -1093,7 +1104,7 @@ __device__ __forceinline__ void run_tile(const LaunchArgs &args, uint32_t epoch,
     int sb = pb, se = pe, w2 = w;
     int parts = 0;                 // partial sums added by this finalizer
     for (;;) {
-        segment<NRB, W>(G, m0, n0, wave, smem, sb, se, outer);
+        segment<NRB, W>(G, args.control + 2, args.sync_spin_limit, m0, n0, wave, smem, sb, se, outer);
         if (pb > 0) {              // a later part of a split tile
             publish_partial<NRB>(args, epoch, w, wave, outer);
             return;
@@ -1455,8 +1466,7 @@ void plan_cuts(LaunchArgs &a, int nwg)
 }
 
 // Library-owned workspace for one stream: partial-sum slots, their flags,
-// and two control words after the flags (the epoch of the last finished
-// launch and a count of finished workgroups).
+// and kControlWords control words after the flags (see LaunchArgs::control).
 struct Workspace {
     float *partials = nullptr;
     uint32_t *flags = nullptr;
@@ -1498,9 +1508,9 @@ int workspace_for(hipStream_t st, int device, int slots, Workspace *&out)
     }
     e = hipMalloc(reinterpret_cast<void **>(&ws.partials), (size_t)slots * kPartialSlot);
     if (e == hipSuccess)
-        e = hipMalloc(reinterpret_cast<void **>(&ws.flags), ((size_t)slots + 2) * sizeof(uint32_t));
+        e = hipMalloc(reinterpret_cast<void **>(&ws.flags), ((size_t)slots + kControlWords) * sizeof(uint32_t));
     if (e == hipSuccess)
-        e = hipMemsetAsync(ws.flags, 0, ((size_t)slots + 2) * sizeof(uint32_t), st);
+        e = hipMemsetAsync(ws.flags, 0, ((size_t)slots + kControlWords) * sizeof(uint32_t), st);
     if (e != hipSuccess) {
         if (ws.partials)
             (void)hipFree(ws.partials);
@@ -1521,6 +1531,15 @@ int spin_limit()
 {
     const char *e = getenv("NVFP4_SPIN_LIMIT");
     return e != nullptr ? atoi(e) : (1 << 20);
+}
+
+// Polls of an A hand-off wait (NVFP4_SYNC_SPIN_LIMIT overrides the default;
+// a tiny value forces the waits to run out: a test of their error word).
+int sync_spin_limit()
+{
+    const char *e = getenv("NVFP4_SYNC_SPIN_LIMIT");
+    const int v = e != nullptr ? atoi(e) : kSyncSpinLimit;
+    return v < 0 ? 0 : v;
 }
 
 int device_units(int &device, int &units)
@@ -1553,7 +1572,7 @@ int device_units(int &device, int &units)
 // address).
 constexpr int kStaticSlots = kMaxWorkgroups;
 constexpr size_t kStaticPartialBytes = (size_t)kStaticSlots * kPartialSlot;
-constexpr size_t kStaticBytes = kStaticPartialBytes + ((size_t)kStaticSlots + 64) * sizeof(uint32_t);
+constexpr size_t kStaticBytes = kStaticPartialBytes + ((size_t)kStaticSlots + kControlWords) * sizeof(uint32_t);
 static __device__ __align__(256) uint8_t scratch[kStaticBytes];
 
 // Device address of `scratch` on the current device, looked up once per
@@ -1617,6 +1636,7 @@ int launch_all(const nvfp4_group_t *groups, int ng, hipStream_t st, bool use_sta
         args.num_wg = nwg;
         plan_cuts(args, nwg);
         args.spin_limit = spin_limit();
+        args.sync_spin_limit = sync_spin_limit();
         hipLaunchKernelGGL((nvfp4_group_gemm_kernel<kWaves>), dim3((unsigned)nwg), dim3(kThreads), 0, st, args);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
@@ -1726,6 +1746,44 @@ extern "C" int nvfp4_release_workspace(void *stream)
     (void)hipFree(it->second.flags);
     g_ws.erase(it);
     return NVFP4_OK;
+}
+
+extern "C" int nvfp4_stream_errors(void *stream)
+{
+    g_err[0] = '\0';
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    int device = 0;
+    hipError_t e = hipGetDevice(&device);
+    if (e != hipSuccess)
+        return -fail(NVFP4_EHIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    e = hipStreamSynchronize(st);
+    if (e != hipSuccess)
+        return -fail(NVFP4_EHIP, "stream synchronize failed: %s", hipGetErrorString(e));
+    uint32_t *words[2] = {nullptr, nullptr};
+    {
+        std::lock_guard<std::mutex> lock(g_ws_mutex);
+        auto it = g_ws.find({device, st});
+        if (it != g_ws.end())
+            words[0] = it->second.flags + it->second.slots + 2;
+    }
+    uint8_t *base = nullptr;
+    if (static_scratch(device, base) == NVFP4_OK)
+        words[1] = reinterpret_cast<uint32_t *>(base + kStaticPartialBytes) + kStaticSlots + 2;
+    long long total = 0;
+    for (uint32_t *w : words) {
+        if (w == nullptr)
+            continue;
+        uint32_t v = 0;
+        e = hipMemcpy(&v, w, sizeof v, hipMemcpyDeviceToHost);
+        if (e == hipSuccess && v != 0) {
+            const uint32_t zero = 0;
+            e = hipMemcpy(w, &zero, sizeof zero, hipMemcpyHostToDevice);
+        }
+        if (e != hipSuccess)
+            return -fail(NVFP4_EHIP, "reading the error word failed: %s", hipGetErrorString(e));
+        total += v;
+    }
+    return total > 0x7fffffff ? 0x7fffffff : (int)total;
 }
 
 extern "C" const char *nvfp4_last_error(void) { return g_err; }

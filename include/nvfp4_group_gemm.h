@@ -150,6 +150,20 @@ int nvfp4_plan(const nvfp4_group_t *groups, int ng, int num_workgroups, int32_t 
  */
 int nvfp4_release_workspace(void *stream);
 
+/*
+ * Waits for the work queued on `stream`, then returns (and clears) the number
+ * of internal hand-off waits that ran out since the last call, counted in
+ * the workspace of (current device, stream) and in the device's
+ * allocation-free workspace.  Inside a workgroup the waves hand decoded A
+ * operands to each other through LDS counters with a bounded wait; a wait
+ * that runs out (never expected: it would mean a bug, and the affected
+ * outputs are then wrong) is counted here instead of hanging the GPU.  The
+ * environment variable NVFP4_SYNC_SPIN_LIMIT (read at each call of the GEMM)
+ * sets the polls of that wait; a tiny value forces it to run out (a test of
+ * this path).  Returns the count (>= 0) or a negated NVFP4 code.
+ */
+int nvfp4_stream_errors(void *stream);
+
 /* Largest row and column extent of one tile. */
 int nvfp4_tile_rows(void);
 int nvfp4_tile_cols(void);

@@ -30,4 +30,6 @@ def run_gpu(groups, stream=None) -> List[np.ndarray]:
     args = device_args(groups)
     nv.group_gemm(args, stream=stream)
     torch.cuda.synchronize()
+    st = stream if stream is not None else torch.cuda.current_stream()
+    assert nv.stream_errors(st.cuda_stream) == 0, "a hand-off wait ran out"
     return [a[4].cpu().numpy().view(np.uint16) for a in args]

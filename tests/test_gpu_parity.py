@@ -182,3 +182,30 @@ def test_config1_recomputed_parts_full():
             os.environ.pop("NVFP4_SPIN_LIMIT", None)
         else:
             os.environ["NVFP4_SPIN_LIMIT"] = old
+
+
+def test_handoff_timeouts_are_counted():
+    """Forcing the waves' A hand-off waits to give up at once
+    (NVFP4_SYNC_SPIN_LIMIT=0; the kernel still exits normally, only its sums
+    may be wrong) is reported by nvfp4_stream_errors, which then reads zero
+    again; a normal call afterwards reports nothing."""
+    import os
+    import torch
+    import block_scaled_fp4_group_amd as nv
+    from tests.gpu_util import device_args
+    groups = workloads.generate(workloads.CONFIGS[3])
+    log("gpu case: forced hand-off timeouts shapes=%s" % [(g.m, g.n, g.k) for g in groups])
+    args = device_args(groups)
+    sid = torch.cuda.current_stream().cuda_stream
+    old = os.environ.get("NVFP4_SYNC_SPIN_LIMIT")
+    os.environ["NVFP4_SYNC_SPIN_LIMIT"] = "0"
+    try:
+        nv.group_gemm(args)
+    finally:
+        if old is None:
+            os.environ.pop("NVFP4_SYNC_SPIN_LIMIT", None)
+        else:
+            os.environ["NVFP4_SYNC_SPIN_LIMIT"] = old
+    assert nv.stream_errors(sid) > 0
+    assert nv.stream_errors(sid) == 0
+    check_full(workloads.generate(workloads.CONFIGS[0]), "after forced timeouts")
