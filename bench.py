@@ -3,17 +3,29 @@
 
 Times the HIP library on the 8-group MoE-like workload (N = 4096, K = 7168,
 M = 80, 176, 128, 72, 64, 248, 96, 160) with seeded synthetic inputs resident
-in HBM, and prints one JSON line: TFLOP/s (2*sum(MNK)/t), the roofline of the
-kernel (algorithmic bytes / measured kernel time against 8 TB/s HBM), and the
-CPU oracle timed on a bounded sample as a baseline.
+in HBM, and prints one JSON line with:
+- TFLOP/s (2*sum(MNK)/t);
+- the roofline of the kernel (algorithmic bytes / mean kernel time from HIP
+  events on the launch stream, against 8 TB/s HBM);
+- the same figures for every one of the five workloads (`config.per_workload`),
+  each also as a fraction of the dense f16 MFMA peak the kernel computes on;
+- the host cost of one call and of one graph replay of the small workload;
+- the CPU oracle timed on a bounded sample as a baseline.
 
 Cold-cache protocol: each step runs on one of R input/output replicas in
 rotation, with R chosen so the replicas together exceed twice the 256 MB
 Infinity Cache; a step never finds its operands in any cache.
+
+Other modes: --mfma-rates prints the measured sustained matrix-core rates and
+clock; --summarize-trace FILE turns a rocprofv3 kernel trace of a default run
+into per-workload kernel times; --oracle-timing times the oracle on every
+workload.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import ctypes
 import hashlib
 import json
 import os
@@ -31,19 +43,27 @@ import workloads  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"fp4": 10100.0, "fp8": 5000.0, "f16": 2500.0}
 MALL_BYTES = 256 << 20
+HEADLINE = 1                   # index of the 8-group N=4096 K=7168 workload
+PER_WORKLOAD_STEPS = 20
+PER_WORKLOAD_WARMUP = 5
+HOST_CALLS = 200
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--config", type=int, default=1, help="workload index (default: the 8-group N=4096 K=7168 case)")
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", type=int, default=HEADLINE,
+                   help="workload of the headline figures (default: the 8-group N=4096 K=7168 case)")
     p.add_argument("--warm-cache", action="store_true", help="reuse one replica (numbers labelled warm)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--all-configs", action="store_true", help="also report every workload on stderr")
+    p.add_argument("--headline-only", action="store_true", help="skip the per-workload array")
     p.add_argument("--oracle-timing", action="store_true",
                    help="time the oracle on every workload with 1 thread and with all threads, then exit")
+    p.add_argument("--mfma-rates", action="store_true", help="measure sustained MFMA rates and clock, then exit")
+    p.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
+                   help="per-workload kernel times from a rocprofv3 kernel trace of a default run, then exit")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                    help="run one plain device-to-device copy of BYTES first (counter calibration)")
     return p.parse_args()
@@ -79,6 +99,16 @@ def measured_traffic(workload_name):
         return None
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def build_replicas(groups, reps, dev):
     import torch
     base = []
@@ -97,7 +127,17 @@ def build_replicas(groups, reps, dev):
     return replicas
 
 
+def launches_per_step(w):
+    """Kernel launches of one call (one per batch of up to 32 non-empty groups)."""
+    n = sum(1 for (m, n_, k) in w.shapes if m and n_)
+    return max(1, -(-n // 32))
+
+
 def time_workload(w, steps, warmup, warm_cache):
+    """Protocol of one workload (the trace summary relies on its launch
+    order): `warmup` untimed calls, `steps` timed calls bracketed by one
+    event pair on the launch stream (and host wall time), then `steps`
+    single calls each bracketed by its own events."""
     import torch
     import block_scaled_fp4_group_amd as nv
     dev = torch.device("cuda:0")
@@ -112,9 +152,6 @@ def time_workload(w, steps, warmup, warm_cache):
     for i in range(warmup):
         nv.group_gemm_raw(descs[i % reps], sid)
     torch.cuda.synchronize()
-    # timed region: exactly `steps` launches, one event pair on the launch
-    # stream around all of them (per-launch events would add their own
-    # dispatch overhead to every launch)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -125,16 +162,54 @@ def time_workload(w, steps, warmup, warm_cache):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     batch_ms = e0.elapsed_time(e1) / steps
-    # distribution of single launches, measured after the timed region
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for i in range(steps):
         ev[i][0].record(stream)
         nv.group_gemm_raw(descs[i % reps], sid)
         ev[i][1].record(stream)
     torch.cuda.synchronize()
-    per = np.array([a.elapsed_time(b) for a, b in ev])       # ms, one launch each
+    if nv.stream_errors(sid) != 0:
+        raise RuntimeError("bench.py: a hand-off wait ran out during %s" % w.name)
+    per = np.array([a.elapsed_time(b) for a, b in ev])       # ms, one call each
     return dict(groups=groups, flops=flops, nbytes=nbytes, reps=reps, wall_ms=wall * 1e3 / steps,
-                ev_ms_mean=float(batch_ms), ev_ms_median=float(np.median(per)), ev_ms_min=float(per.min()))
+                ev_ms_mean=float(batch_ms), ev_ms_median=float(np.median(per)), ev_ms_min=float(per.min()),
+                launches=launches_per_step(w))
+
+
+def host_and_graph_cost(w):
+    """Host time of one call (argument marshalling, plan cache hit, launch)
+    measured over HOST_CALLS back-to-back calls without synchronising, and
+    the device time of one replay of a captured call."""
+    import torch
+    import block_scaled_fp4_group_amd as nv
+    dev = torch.device("cuda:0")
+    groups = workloads.generate(w)
+    rep = build_replicas(groups, 1, dev)[0]
+    descs = [nv._descriptor(*g) for g in rep]
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        for _ in range(5):
+            nv.group_gemm_raw(descs, s.cuda_stream)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(HOST_CALLS):
+            nv.group_gemm_raw(descs, s.cuda_stream)
+        host_us = (time.perf_counter() - t0) / HOST_CALLS * 1e6
+        torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        nv.group_gemm_raw(descs, s.cuda_stream)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(HOST_CALLS):
+        g.replay()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return round(host_us, 2), round(e0.elapsed_time(e1) / HOST_CALLS * 1e3, 2)
 
 
 def roofline(flops, nbytes, seconds, traffic=None):
@@ -143,8 +218,7 @@ def roofline(flops, nbytes, seconds, traffic=None):
     flops) per launch / mean launch time."""
     t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
     t_fp4 = flops / (MFMA_PEAK_TFLOPS["fp4"] * 1e12)
-    bound = "hbm" if t_hbm >= t_fp4 else "mfma"
-    if bound == "hbm":
+    if t_hbm >= t_fp4:
         ach = nbytes / seconds / 1e9
         return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic}
@@ -152,6 +226,18 @@ def roofline(flops, nbytes, seconds, traffic=None):
     pk = MFMA_PEAK_TFLOPS["fp4"]
     return {"bound": "mfma", "achieved": round(ach, 1), "peak": pk, "unit": "TFLOP/s",
             "frac": round(ach / pk, 4), "traffic": traffic}
+
+
+def workload_entry(w, r, warm_cache):
+    s = r["ev_ms_mean"] * 1e-3
+    tf = r["flops"] / s / 1e12
+    rf = roofline(r["flops"], r["nbytes"], s)
+    return {"workload": w.name, "us": round(s * 1e6, 2), "tflops": round(tf, 2),
+            "gbs": round(r["nbytes"] / s / 1e9, 1), "bound": rf["bound"], "roofline_frac": rf["frac"],
+            "hbm_frac": round(r["nbytes"] / s / 1e9 / HBM_PEAK_GBS, 4),
+            "f16_mfma_frac": round(tf / MFMA_PEAK_TFLOPS["f16"], 4),
+            "single_call_us_median": round(r["ev_ms_median"] * 1e3, 2),
+            "cache": "warm" if warm_cache else "cold (%d replicas)" % r["reps"]}
 
 
 def cpu_baseline(w, groups, budget_s=20.0):
@@ -169,7 +255,8 @@ def cpu_baseline(w, groups, budget_s=20.0):
         if dt >= budget_s:
             break
     return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.max_threads(),
-            "kind": "oracle", "sample": "full fp64 oracle GEMM of %d of %d groups of %s (%.2f GFLOP), %.1f s wall"
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": "full fp64 oracle GEMM of %d of %d groups of %s (%.2f GFLOP), %.1f s wall"
             % (used, len(groups), w.name, fl / 1e9, dt)}
 
 
@@ -186,11 +273,70 @@ def oracle_timing():
                 oracle.gemm_group(g.a, g.sfa, g.b, g.sfb, g.m, g.n, g.k, nt)
             dt = time.perf_counter() - t0
             print(json.dumps({"workload": w.name, "threads": nt, "seconds": round(dt, 3),
-                              "tflops": round(flops / dt / 1e12, 6), "kind": "oracle"}), flush=True)
+                              "tflops": round(flops / dt / 1e12, 6), "kind": "oracle",
+                              "cpu_model": cpu_model()}), flush=True)
+
+
+def mfma_rates():
+    import torch
+    torch.cuda.init()
+    path = os.path.join(_REPO, "block_scaled_fp4_group_amd", "libnvfp4gg_probe.so")
+    if not os.path.exists(path):
+        raise RuntimeError("libnvfp4gg_probe.so is not built; run __graft_entry__.build()")
+    L = ctypes.CDLL(path)
+    L.nvfp4_probe_mfma_rates.restype = ctypes.c_int
+    L.nvfp4_probe_mfma_rates.argtypes = [ctypes.c_char_p, ctypes.c_int]
+    buf = ctypes.create_string_buffer(8192)
+    rc = L.nvfp4_probe_mfma_rates(buf, 8192)
+    sys.stdout.write(buf.value.decode())
+    if rc != 0:
+        raise RuntimeError("mfma rate probe: a HIP call failed")
+
+
+def trace_protocol(steps, warmup, headline_only, config=HEADLINE):
+    """Kernel launches of a run in order: (label, count) blocks, the timed
+    regions marked."""
+    blocks = []
+
+    def add(w, st, wu):
+        n = launches_per_step(w)
+        blocks.append((w.name + " warmup", wu * n, False))
+        blocks.append((w.name + " timed", st * n, True))
+        blocks.append((w.name + " single", st * n, False))
+    add(workloads.CONFIGS[config], steps, warmup)
+    if not headline_only:
+        for w in workloads.CONFIGS:
+            add(w, PER_WORKLOAD_STEPS, PER_WORKLOAD_WARMUP)
+    return blocks
+
+
+def summarize_trace(path, steps, warmup, headline_only, config=HEADLINE):
+    """Mean kernel duration per timed region of a rocprofv3 --kernel-trace
+    CSV of `bench.py --steps S --warmup W` (the GEMM kernel's dispatches in
+    order; graph replays and host-cost calls come after the blocks)."""
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if "nvfp4_group_gemm_kernel" in r.get("Kernel_Name", ""):
+                rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    rows.sort()
+    durs = [(e - s) / 1e3 for s, e in rows]
+    i = 0
+    print("kernel dispatches in trace: %d" % len(durs))
+    for label, n, timed in trace_protocol(steps, warmup, headline_only, config):
+        seg = durs[i:i + n]
+        i += n
+        if timed and seg:
+            print("%-48s launches %3d  mean %8.2f us  median %8.2f us  min %8.2f us"
+                  % (label, len(seg), float(np.mean(seg)), float(np.median(seg)), float(np.min(seg))))
+    print("remaining dispatches (host-cost calls, graph replays): %d" % max(0, len(durs) - i))
 
 
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.steps, args.warmup, args.headline_only, args.config)
+        return
     if args.oracle_timing:
         oracle_timing()
         return
@@ -203,6 +349,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.mfma_rates:
+        mfma_rates()
+        return
     w = workloads.CONFIGS[args.config]
     if args.calibrate_copy > 0:
         n = args.calibrate_copy // 4
@@ -216,6 +365,16 @@ def main():
     r = time_workload(w, args.steps, args.warmup, args.warm_cache)
     kern_s = r["ev_ms_mean"] * 1e-3
     tflops = r["flops"] / (r["wall_ms"] * 1e-3) / 1e12     # whole-job rate over the timed steps
+    per_workload = []
+    if not args.headline_only:
+        for wc in workloads.CONFIGS:
+            rc = time_workload(wc, PER_WORKLOAD_STEPS, PER_WORKLOAD_WARMUP, args.warm_cache)
+            per_workload.append(workload_entry(wc, rc, args.warm_cache))
+            del rc
+            torch.cuda.empty_cache()
+        host_us, graph_us = host_and_graph_cost(workloads.CONFIGS[0])
+        per_workload[0]["host_us_per_call"] = host_us
+        per_workload[0]["graph_replay_us"] = graph_us
     line = {
         "metric": "grouped NVFP4 GEMM TFLOP/s (2*sum(MNK)/t) and % of binding roofline, 1 MI355X",
         "value": round(tflops, 2),
@@ -234,21 +393,14 @@ def main():
                    "gflop": round(r["flops"] / 1e9, 3), "alg_bytes_mb": round(r["nbytes"] / 1e6, 3),
                    "kernel_ms_mean": round(r["ev_ms_mean"], 5),
                    "single_launch_ms_median": round(r["ev_ms_median"], 5),
-                   "single_launch_ms_min": round(r["ev_ms_min"], 5)},
+                   "single_launch_ms_min": round(r["ev_ms_min"], 5),
+                   "f16_mfma_frac": round(r["flops"] / kern_s / 1e12 / MFMA_PEAK_TFLOPS["f16"], 4),
+                   "per_workload": per_workload},
         "roofline": roofline(r["flops"], r["nbytes"], kern_s,
                              None if args.warm_cache else measured_traffic(w.name)),
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, r["groups"])
-    if args.all_configs:
-        for i, wc in enumerate(workloads.CONFIGS):
-            rc = time_workload(wc, max(10, args.steps // 2), 5, args.warm_cache)
-            s = rc["ev_ms_mean"] * 1e-3
-            rf = roofline(rc["flops"], rc["nbytes"], s)
-            print(json.dumps({"workload": wc.name, "us": round(s * 1e6, 2),
-                              "tflops": round(rc["flops"] / s / 1e12, 2),
-                              "gbs": round(rc["nbytes"] / s / 1e9, 1), "roofline": rf,
-                              "cache": "warm" if args.warm_cache else "cold"}), file=sys.stderr, flush=True)
     print(json.dumps(line), flush=True)
 
 

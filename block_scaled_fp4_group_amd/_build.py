@@ -9,6 +9,9 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 REPO_DIR = os.path.dirname(PKG_DIR)
 SRC = os.path.join(PKG_DIR, "csrc", "nvfp4_group_gemm.hip")
 LIB = os.path.join(PKG_DIR, "libnvfp4gg.so")
+# measurement probe (matrix-core rates and clock), loaded by bench.py only
+PROBE_SRC = os.path.join(PKG_DIR, "csrc", "mfma_rate.hip")
+PROBE_LIB = os.path.join(PKG_DIR, "libnvfp4gg_probe.so")
 INCLUDE = os.path.join(REPO_DIR, "include")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -22,15 +25,22 @@ FLAGS = [
 ]
 
 
-def build_library(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, "-I" + INCLUDE, SRC, "-o", tmp]
+def _compile(src: str, lib: str, verbose: bool) -> str:
+    tmp = lib + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *FLAGS, "-I" + INCLUDE, src, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+    return lib
+
+
+def build_library(verbose: bool = False) -> str:
+    """The GEMM library, then the measurement probe."""
+    _compile(SRC, LIB, verbose)
+    _compile(PROBE_SRC, PROBE_LIB, verbose)
     return LIB
 
 
