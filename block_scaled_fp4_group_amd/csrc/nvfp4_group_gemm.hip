@@ -974,13 +974,33 @@ __device__ __forceinline__ Exact2 exact2(const uint8_t *a, const uint8_t *sfa, c
     return r;
 }
 
+// Exact values of the n outputs listed in lanes 0..n-1 (row lrow, column
+// lcol of one group), rounded to fp16 and stored over what the tile's store
+// wrote there (the same wave's later store to the same address wins).  One
+// copy for every tile height: the caller's sums are no longer live here.
+__device__ __noinline__ void store_exact(const uint8_t *a, const uint8_t *sfa, const uint8_t *b, const uint8_t *sfb,
+                                         _Float16 *c, int M, int N, int K, int lrow, int lcol, int n)
+{
+    const int lane = threadIdx.x & 63;
+    for (int p = 0; p < n; p += 2) {
+        const int p1 = p + 1 < n ? p + 1 : p;
+        const int r0 = __builtin_amdgcn_readlane(lrow, p), c0 = __builtin_amdgcn_readlane(lcol, p);
+        const int r1 = __builtin_amdgcn_readlane(lrow, p1), c1 = __builtin_amdgcn_readlane(lcol, p1);
+        const Exact2 x = exact2(a, sfa, b, sfb, M, N, K, r0, c0, r1, c1);
+        if (lane == 0)
+            c[(size_t)r0 * N + c0] = (_Float16)(float)x.v[0];
+        if (lane == 1)
+            c[(size_t)r1 * N + c1] = (_Float16)(float)x.v[1];
+    }
+}
+
 // The check and the exact recomputation for one finished tile (see above);
 // `parts` is the number of partial sums the finalizer added.  Lane (r, q)
 // holds outer[i][cb][e] = C[m0 + 16 i + 4 q + e][n0 + 32 wave + 16 cb + r].
-// The outputs at risk are visited twice in the same order: the first pass
-// lists them (position p of the list in lane p) and their exact values are
-// computed two at a time; the second pass writes each back to its lane.
-// More than 64 at risk take further rounds.
+// The outputs at risk are listed (position p of the list in lane p) and
+// their exact values stored over the tile's stored fp16 values, two at a
+// time; more than 64 at risk take further rounds.  Called after the tile's
+// store.
 template <int NRB>
 __device__ __forceinline__ void fix_small_outputs(const GroupArgs &G, int m0, int rows, int n0, int wave, int parts,
                                                   f32x4 (&outer)[NRB][2])
@@ -1027,7 +1047,8 @@ __device__ __forceinline__ void fix_small_outputs(const GroupArgs &G, int m0, in
         return row < row_end && col_base + 16 * cb < G.n && __builtin_fabsf(outer[i][cb][e]) < thresh;
     };
     for (int round = 0;; ++round) {
-        // pass 1: list entries [64 round, 64 round + 64) in lanes 0..63
+        // entries [64 round, 64 round + 64) of the outputs at risk, listed
+        // in lanes 0..63 in a fixed visit order
         int lrow = 0, lcol = 0, n = 0, seen = 0;
 #pragma unroll
         for (int i = 0; i < NRB; ++i)
@@ -1051,35 +1072,8 @@ __device__ __forceinline__ void fix_small_outputs(const GroupArgs &G, int m0, in
                 }
         if (n == 0)
             return;
-        // exact values, two at a time (a short last batch repeats its entry)
-        double lval = 0.0;
-        for (int p = 0; p < n; p += 2) {
-            const int p1 = p + 1 < n ? p + 1 : p;
-            const Exact2 x = exact2(G.a, G.sfa, G.b, G.sfb, G.m, G.n, G.k, __builtin_amdgcn_readlane(lrow, p),
-                                    __builtin_amdgcn_readlane(lcol, p), __builtin_amdgcn_readlane(lrow, p1),
-                                    __builtin_amdgcn_readlane(lcol, p1));
-            lval = lane == p ? x.v[0] : lval;
-            lval = lane == p1 ? x.v[1] : lval;
-        }
-        // pass 2: the same visit order; entry k goes back to its owner
-        int k = 0;
-#pragma unroll
-        for (int i = 0; i < NRB; ++i)
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const bool risk = at_risk(i, cb, e);
-                    uint64_t todo = __ballot(risk);
-                    // this lane's rank among the set lanes of this element
-                    const int below = __builtin_popcountll(todo & ((1ull << lane) - 1));
-                    const int idx = k + below - 64 * round;
-                    const double v = __shfl(lval, idx & 63);
-                    if (risk && idx >= 0 && idx < n)
-                        outer[i][cb][e] = (float)v;
-                    k += __builtin_popcountll(todo);
-                }
-        if (n < 64)
+        store_exact(G.a, G.sfa, G.b, G.sfb, G.c, G.m, G.n, G.k, lrow, lcol, n);
+        if (seen <= 64 * (round + 1))
             return;
     }
 }
@@ -1135,8 +1129,8 @@ __device__ __forceinline__ void run_tile(const LaunchArgs &args, uint32_t epoch,
             break;
         ++parts;                   // the recomputed part restarts its sums too
     }
-    fix_small_outputs<NRB>(G, m0, rows, n0, wave, parts, outer);
     store_tile<NRB>(G, m0, rows, n0, wave, outer);
+    fix_small_outputs<NRB>(G, m0, rows, n0, wave, parts, outer);
 }
 
 template <int W>
