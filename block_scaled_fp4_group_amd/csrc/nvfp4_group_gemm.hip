@@ -107,6 +107,17 @@ struct GroupArgs {
     int64_t cost_begin;  // cost before this group's first tile
 };
 
+// Where one workgroup's range starts: its logical index w (workgroups are
+// dealt round-robin to the XCDs, and consecutive logical ranges share A rows
+// and B columns, so the host maps block b to w = (b % 8) (num_wg / 8) + b / 8
+// when num_wg % 8 == 0), its first tile and pair (pack_start) and the end of
+// its pairs in that tile (pe = 0: no work).
+struct WgStart {
+    uint64_t pos;
+    int32_t w;
+    int32_t pe;
+};
+
 struct LaunchArgs {
     GroupArgs g[kMaxGroupsPerLaunch];
     // g[i].cost_begin again, contiguous (INT64_MAX past the last group), so
@@ -129,8 +140,10 @@ struct LaunchArgs {
     // pairs whose end cost lies in it belong to w (cut[0] = 0, cut[num_wg] =
     // total_cost, non-decreasing; chosen on the host)
     int64_t cut[kMaxWorkgroups + 1];
-    // workgroup w's first tile and pair (pack_start), found by the host
-    uint64_t start[kMaxWorkgroups];
+    // indexed by blockIdx.x: the logical workgroup it runs and where its
+    // range starts, found by the host so that a workgroup reaches its first
+    // loads of operand data after two dependent rounds of argument loads
+    WgStart first[kMaxWorkgroups];
 };
 
 __host__ __device__ inline int pair_cost(int nrb, int npairs)
@@ -244,15 +257,10 @@ __host__ __device__ inline uint64_t pack_start(const TilePos &p, int ng)
     return (uint64_t)p.pair | (uint64_t)p.rt << 20 | (uint64_t)p.strip << 38 | (uint64_t)p.g << 58;
 }
 
-__host__ __device__ inline TilePos unpack_start(const LaunchArgs &args, uint64_t v)
+// The position packed by pack_start (its cost fields are set by finish_pos).
+__host__ __device__ inline TilePos unpack_pos(uint64_t v)
 {
-    TilePos p{(int)(v >> 58), (int)((v >> 38) & 0xFFFFF), (int)((v >> 20) & 0x3FFFF), (int)(v & 0xFFFFF),
-              args.total_cost, 1, 1};
-    if (p.g < args.ng)
-        finish_pos(args.g[p.g], p);
-    else
-        p.g = args.ng;
-    return p;
+    return TilePos{(int)(v >> 58), (int)((v >> 38) & 0xFFFFF), (int)((v >> 20) & 0x3FFFF), (int)(v & 0xFFFFF), 0, 1, 1};
 }
 
 // Pairs [*pb, *pe) of the tile at p whose end cost lies in (lo, hi].
@@ -900,111 +908,185 @@ __device__ __forceinline__ float code_dot8_f16(uint32_t xa, uint32_t xb, float a
     return acc;
 }
 
-// Exact values of two outputs (rows m[j], columns n[j] of one group; a
-// repeated pair is fine).  Per 16-k block the sum of the 16 code products is
-// exact in fp32 (multiples of 1/4, |sum| <= 576), and so is its product with
-// both block scales (at most 20 significant bits); the blocks are summed in
-// fp64.  Lane l takes blocks 4 l .. 4 l + 3 of every 256-block pass, so a
-// pass issues every load of both outputs before waiting for any (one pass
-// for K <= 4096); the wave's partial sums are combined at the end and every
-// lane returns the totals.
-struct Exact2 {
-    double v[2];
-};
-
-__device__ __forceinline__ Exact2 exact2(const uint8_t *a, const uint8_t *sfa, const uint8_t *b, const uint8_t *sfb,
-                                         int M, int N, int K, int m0, int n0, int m1, int n1)
+// f64 -> fp16 rounded once: the value is first rounded to f32 with round-to-
+// odd (truncation, with the last bit set when anything was dropped), which
+// keeps enough to let the f32 -> fp16 rounding to nearest-even decide as a
+// direct rounding would.
+__device__ __forceinline__ _Float16 f64_to_f16(double x)
 {
-    const int lane = threadIdx.x & 63;
+    float f = (float)x;
+    if (__builtin_isfinite(f) && (double)f != x) {
+        uint32_t u = __builtin_bit_cast(uint32_t, f);
+        if (__builtin_fabs((double)f) > __builtin_fabs(x))
+            u -= 1u;               // the value truncated toward zero
+        f = __builtin_bit_cast(float, u | 1u);
+    }
+    return (_Float16)f;
+}
+
+// f64 value of lane (lane ^ pattern) for a DPP lane pattern.
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x)
+{
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+    return __builtin_bit_cast(double, (uint64_t)hi << 32 | lo);
+}
+
+__device__ __forceinline__ double readlane_f64(double x, int l)
+{
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+    return __builtin_bit_cast(double, (uint64_t)hi << 32 | lo);
+}
+
+// Exact values of the n outputs listed in lanes 0..n-1 (row lrow, column
+// lcol of one group), rounded once to fp16 and stored over what the tile's
+// store wrote there (the same wave's later store to the same address wins).
+// Per 16-k block the sum of the 16 code products is exact in fp32 (multiples
+// of 1/4, |sum| <= 576), and so is its product with both block scales (at
+// most 20 significant bits); the blocks are summed in fp64.
+// Outputs are taken eight at a time; each of a batch's outputs gets L = 64 /
+// (batch size rounded up to a power of two, at least 8) lanes, and lane s
+// of an output takes blocks 4 s + 4 L t + [0, 4) for t = 0, 1, ...  The
+// loads of four such steps are issued one group ahead of the arithmetic, so
+// one memory latency covers most of a batch.  The L lanes' sums are then
+// combined (DPP within 16 lanes, lane reads beyond) and lane 0 of each
+// output stores it.  kCompact: one step per load group and no loads ahead,
+// for the out-of-line copy, which must fit in few registers.
+template <bool kCompact>
+__device__ __forceinline__ void store_exact(const uint8_t *a, const uint8_t *sfa, const uint8_t *b, const uint8_t *sfb,
+                                            _Float16 *c, int M, int N, int K, int lrow, int lcol, int n)
+{
+    const int lane = lane_id();
     const int nb = K >> 4;
     const uint32_t row_bytes = (uint32_t)K >> 1, row_sc = (uint32_t)K >> 4;
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void *)a, 0, M * (int)row_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void *)b, 0, N * (int)row_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc((void *)sfa, 0, M * (int)row_sc, 0x00020000);
     const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc((void *)sfb, 0, N * (int)row_sc, 0x00020000);
-    const int mm[2] = {m0, m1}, nn[2] = {n0, n1};
-    double acc[2] = {0.0, 0.0};
-    for (int base = 0; base < nb; base += 256) {
-        const int blk = base + 4 * lane;   // nb % 4 == 0: a lane's four blocks are all in or all out
-        const bool in = blk < nb;
-        u32x4 ca[2][2], cb[2][2];
-        uint32_t sa[2], sb[2];
+    for (int base = 0; base < n; base += 8) {
+        const int cnt = n - base < 8 ? n - base : 8;
+        const int lg = cnt == 1 ? 6 : (cnt == 2 ? 5 : (cnt <= 4 ? 4 : 3));   // log2 of the lanes per output
+        const int L = 1 << lg;
+        const int j = lane >> lg, sl = lane & (L - 1);
+        const int idx = base + (j < cnt ? j : cnt - 1);     // spare lanes repeat the batch's last output
+        const uint32_t row = (uint32_t)__builtin_amdgcn_ds_bpermute(idx << 2, lrow);
+        const uint32_t col = (uint32_t)__builtin_amdgcn_ds_bpermute(idx << 2, lcol);
+        const int steps = (nb + 4 * L - 1) / (4 * L);       // 4-block steps of one lane
+        constexpr int kSteps = kCompact ? 1 : 4;             // steps per load group
+        constexpr int kBufs = kCompact ? 1 : 2;
+        const int groups = (steps + kSteps - 1) / kSteps;
+        u32x4 ca[kBufs][kSteps][2], cb[kBufs][kSteps][2];
+        uint32_t sa[kBufs][kSteps], sb[kBufs][kSteps];
+        // group g's loads into buffer buf; steps past the lane's blocks load
+        // from offset 0 (in bounds) and are not summed
+        auto load = [&](auto buf_t, int g) {
+            constexpr int buf = decltype(buf_t)::value;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const uint32_t oa = (uint32_t)mm[j] * row_bytes + 8u * (uint32_t)blk;
-            const uint32_t ob = (uint32_t)nn[j] * row_bytes + 8u * (uint32_t)blk;
-            ca[j][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, oa, 0, 0));
-            ca[j][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, oa + 16u, 0, 0));
-            cb[j][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, ob, 0, 0));
-            cb[j][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, ob + 16u, 0, 0));
-            sa[j] = __builtin_amdgcn_raw_buffer_load_b32(rsa, (uint32_t)mm[j] * row_sc + (uint32_t)blk, 0, 0);
-            sb[j] = __builtin_amdgcn_raw_buffer_load_b32(rsb, (uint32_t)nn[j] * row_sc + (uint32_t)blk, 0, 0);
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            float prod[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const u32x4 &xa = ca[j][t >> 1], &xb = cb[j][t >> 1];
-                const int d = 2 * (t & 1);
-                prod[t] = code_dot8_f16(xa[d + 1], xb[d + 1], code_dot8_f16(xa[d], xb[d], 0.0f));
+            for (int t = 0; t < kSteps; ++t) {
+                const int blk = 4 * sl + 4 * L * (kSteps * g + t);
+                const uint32_t bo = blk < nb ? (uint32_t)blk : 0u;
+                const uint32_t oa = row * row_bytes + 8u * bo, ob = col * row_bytes + 8u * bo;
+                ca[buf][t][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, oa, 0, 0));
+                ca[buf][t][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, oa + 16u, 0, 0));
+                cb[buf][t][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, ob, 0, 0));
+                cb[buf][t][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, ob + 16u, 0, 0));
+                sa[buf][t] = __builtin_amdgcn_raw_buffer_load_b32(rsa, row * row_sc + bo, 0, 0);
+                sb[buf][t] = __builtin_amdgcn_raw_buffer_load_b32(rsb, col * row_sc + bo, 0, 0);
             }
-            const float s0 = __builtin_amdgcn_cvt_scalef32_f32_fp8(sa[j], 1.0f, 0) *
-                             __builtin_amdgcn_cvt_scalef32_f32_fp8(sb[j], 1.0f, 0);
-            const float s1 = __builtin_amdgcn_cvt_scalef32_f32_fp8(sa[j], 1.0f, 1) *
-                             __builtin_amdgcn_cvt_scalef32_f32_fp8(sb[j], 1.0f, 1);
-            const float s2 = __builtin_amdgcn_cvt_scalef32_f32_fp8(sa[j], 1.0f, 2) *
-                             __builtin_amdgcn_cvt_scalef32_f32_fp8(sb[j], 1.0f, 2);
-            const float s3 = __builtin_amdgcn_cvt_scalef32_f32_fp8(sa[j], 1.0f, 3) *
-                             __builtin_amdgcn_cvt_scalef32_f32_fp8(sb[j], 1.0f, 3);
-            const double part = (double)(prod[0] * s0) + (double)(prod[1] * s1) + (double)(prod[2] * s2) +
-                                (double)(prod[3] * s3);
-            acc[j] += in ? part : 0.0;
+        };
+        auto sum = [&](auto buf_t, int g) -> double {
+            constexpr int buf = decltype(buf_t)::value;
+            double acc = 0.0;
+#pragma unroll
+            for (int t = 0; t < kSteps; ++t) {
+                const int blk = 4 * sl + 4 * L * (kSteps * g + t);
+                float prod[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const u32x4 &xa = ca[buf][t][q >> 1], &xb = cb[buf][t][q >> 1];
+                    const int d = 2 * (q & 1);
+                    prod[q] = code_dot8_f16(xa[d + 1], xb[d + 1], code_dot8_f16(xa[d], xb[d], 0.0f));
+                }
+                const float s0 = __builtin_amdgcn_cvt_scalef32_f32_fp8(sa[buf][t], 1.0f, 0) *
+                                 __builtin_amdgcn_cvt_scalef32_f32_fp8(sb[buf][t], 1.0f, 0);
+                const float s1 = __builtin_amdgcn_cvt_scalef32_f32_fp8(sa[buf][t], 1.0f, 1) *
+                                 __builtin_amdgcn_cvt_scalef32_f32_fp8(sb[buf][t], 1.0f, 1);
+                const float s2 = __builtin_amdgcn_cvt_scalef32_f32_fp8(sa[buf][t], 1.0f, 2) *
+                                 __builtin_amdgcn_cvt_scalef32_f32_fp8(sb[buf][t], 1.0f, 2);
+                const float s3 = __builtin_amdgcn_cvt_scalef32_f32_fp8(sa[buf][t], 1.0f, 3) *
+                                 __builtin_amdgcn_cvt_scalef32_f32_fp8(sb[buf][t], 1.0f, 3);
+                const double part = (double)(prod[0] * s0) + (double)(prod[1] * s1) + (double)(prod[2] * s2) +
+                                    (double)(prod[3] * s3);
+                acc += blk < nb ? part : 0.0;
+            }
+            return acc;
+        };
+        std::integral_constant<int, 0> b0;
+        std::integral_constant<int, 1> b1;
+        double acc = 0.0;
+        if constexpr (kCompact) {
+            for (int g = 0; g < groups; ++g) {
+                load(b0, g);
+                acc += sum(b0, g);
+            }
+        } else {
+            load(b0, 0);
+            for (int g = 0; g < groups; g += 2) {
+                load(b1, g + 1);
+                acc += sum(b0, g);
+                if (g + 1 < groups) {
+                    load(b0, g + 2);
+                    acc += sum(b1, g + 1);
+                }
+            }
         }
+        // sum over each output's L lanes: xor 1, xor 2, then the mirrors
+        // within 8 and 16 lanes (each lane already holds its quad's or
+        // half's sum), then lane reads across rows of 16
+        acc += dpp_f64<0xB1>(acc);        // quad_perm [1, 0, 3, 2]
+        acc += dpp_f64<0x4E>(acc);        // quad_perm [2, 3, 0, 1]
+        acc += dpp_f64<0x141>(acc);       // row_half_mirror
+        if (L >= 16)
+            acc += dpp_f64<0x140>(acc);   // row_mirror
+        if (L == 32)
+            acc = j == 0 ? readlane_f64(acc, 0) + readlane_f64(acc, 16) : readlane_f64(acc, 32) + readlane_f64(acc, 48);
+        else if (L == 64)
+            acc = (readlane_f64(acc, 0) + readlane_f64(acc, 16)) + (readlane_f64(acc, 32) + readlane_f64(acc, 48));
+        if (sl == 0 && j < cnt)
+            c[(size_t)row * N + col] = f64_to_f16(acc);
     }
-    Exact2 r;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        double x = acc[j];
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1)
-            x += __shfl_xor(x, off);
-        r.v[j] = x;
-    }
-    return r;
 }
 
-// Exact values of the n outputs listed in lanes 0..n-1 (row lrow, column
-// lcol of one group), rounded to fp16 and stored over what the tile's store
-// wrote there (the same wave's later store to the same address wins).  One
-// copy for every tile height: the caller's sums are no longer live here.
-__device__ __noinline__ void store_exact(const uint8_t *a, const uint8_t *sfa, const uint8_t *b, const uint8_t *sfb,
-                                         _Float16 *c, int M, int N, int K, int lrow, int lcol, int n)
+// The batches of a list beyond its first 64 entries (rare: more than 64
+// outputs of one wave at risk), one copy for every tile height.
+__device__ __noinline__ void store_exact_more(const uint8_t *a, const uint8_t *sfa, const uint8_t *b,
+                                              const uint8_t *sfb, _Float16 *c, int M, int N, int K, int lrow,
+                                              int lcol, int n)
 {
-    const int lane = threadIdx.x & 63;
-    for (int p = 0; p < n; p += 2) {
-        const int p1 = p + 1 < n ? p + 1 : p;
-        const int r0 = __builtin_amdgcn_readlane(lrow, p), c0 = __builtin_amdgcn_readlane(lcol, p);
-        const int r1 = __builtin_amdgcn_readlane(lrow, p1), c1 = __builtin_amdgcn_readlane(lcol, p1);
-        const Exact2 x = exact2(a, sfa, b, sfb, M, N, K, r0, c0, r1, c1);
-        if (lane == 0)
-            c[(size_t)r0 * N + c0] = (_Float16)(float)x.v[0];
-        if (lane == 1)
-            c[(size_t)r1 * N + c1] = (_Float16)(float)x.v[1];
-    }
+    store_exact<true>(a, sfa, b, sfb, c, M, N, K, lrow, lcol, n);
 }
 
-// The check and the exact recomputation for one finished tile (see above);
-// `parts` is the number of partial sums the finalizer added.  Lane (r, q)
-// holds outer[i][cb][e] = C[m0 + 16 i + 4 q + e][n0 + 32 wave + 16 cb + r].
-// The outputs at risk are listed (position p of the list in lane p) and
-// their exact values stored over the tile's stored fp16 values, two at a
-// time; more than 64 at risk take further rounds.  Called after the tile's
-// store.
+// Outputs one wave must recompute after its tile's store: entry p of the
+// list (row, column) in lane p, n entries.
+struct FixList {
+    int lrow, lcol, n;
+};
+
+// The check for one finished tile (see above); `parts` is the number of
+// partial sums the finalizer added.  Lane (r, q) holds outer[i][cb][e] =
+// C[m0 + 16 i + 4 q + e][n0 + 32 wave + 16 cb + r].  The outputs at risk
+// are listed (position p of the list in lane p); the first 64 are returned
+// for the caller to recompute (store_exact), any further ones are
+// recomputed here.  Called after the tile's store.
 template <int NRB>
-__device__ __forceinline__ void fix_small_outputs(const GroupArgs &G, int m0, int rows, int n0, int wave, int parts,
-                                                  f32x4 (&outer)[NRB][2])
+__device__ __forceinline__ FixList fix_small_outputs(const GroupArgs &G, int m0, int rows, int n0, int wave,
+                                                     int parts, f32x4 (&outer)[NRB][2])
 {
+    FixList first{0, 0, 0};
     const int lane = lane_id();
     const int r = lane & 15, q = lane >> 4;
     const int row_end = m0 + rows;
@@ -1037,54 +1119,75 @@ __device__ __forceinline__ void fix_small_outputs(const GroupArgs &G, int m0, in
         ss = 0x1p100f;             // a non-finite sum: every output of the wave is checked exactly
     const float K = (float)G.k;
     const float F = (float)(kFoldStages * kStageK);
-    const float sigma = 0x1p-24f * __builtin_sqrtf(ss / cnt) *
-                        __builtin_sqrtf(fminf(F, K) / 16.0f + K / (2.0f * F) + (float)parts);
-    const float thresh = (kSigmaMargin * sigma - kTolAbs) / kTolRel;   // recompute |c| < thresh
+    const float sigma = 0x1p-24f * __builtin_amdgcn_sqrtf(ss * (1.0f / cnt)) *
+                        __builtin_amdgcn_sqrtf(fminf(F, K) * (1.0f / 16.0f) + K * (0.5f / F) + (float)parts);
+    const float thresh = (kSigmaMargin * sigma - kTolAbs) * (1.0f / kTolRel);   // recompute |c| < thresh
     if (!(thresh > 0.0f))
-        return;
-    auto at_risk = [&](int i, int cb, int e) {
-        const int row = m0 + 16 * i + 4 * q + e;
-        return row < row_end && col_base + 16 * cb < G.n && __builtin_fabsf(outer[i][cb][e]) < thresh;
-    };
-    for (int round = 0;; ++round) {
-        // entries [64 round, 64 round + 64) of the outputs at risk, listed
-        // in lanes 0..63 in a fixed visit order
-        int lrow = 0, lcol = 0, n = 0, seen = 0;
+        return first;
+    // Per lane, bit 2 (4 i + e) + cb of a 64-bit mask (lo: i < 4, hi: i >= 4)
+    // marks an output at risk: a compare and a shift per output.
+    uint32_t risk[2] = {0u, 0u};
 #pragma unroll
-        for (int i = 0; i < NRB; ++i)
+    for (int h = 0; h < (NRB > 4 ? 2 : 1); ++h)
 #pragma unroll
-            for (int cb = 0; cb < 2; ++cb)
+        for (int i = (h + 1) * 4 - 1; i >= h * 4; --i)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    uint64_t todo = __ballot(at_risk(i, cb, e));
-                    while (todo) {
-                        const int owner = __builtin_ctzll(todo);
-                        todo &= todo - 1;
-                        if (seen >= 64 * round && n < 64) {
-                            const int orow = m0 + 16 * i + 4 * (owner >> 4) + e;
-                            const int ocol = n0 + 32 * wave + 16 * cb + (owner & 15);
-                            lrow = lane == n ? orow : lrow;
-                            lcol = lane == n ? ocol : lcol;
-                            ++n;
-                        }
-                        ++seen;
-                    }
-                }
-        if (n == 0)
-            return;
-        store_exact(G.a, G.sfa, G.b, G.sfb, G.c, G.m, G.n, G.k, lrow, lcol, n);
-        if (seen <= 64 * (round + 1))
-            return;
+            for (int e = 3; e >= 0; --e)
+#pragma unroll
+                for (int cb = 1; cb >= 0; --cb)
+                    if (i < NRB)
+                        risk[h] = 2u * risk[h] + (__builtin_fabsf(outer[i][cb][e]) < thresh ? 1u : 0u);
+    // rows past the tile: (i, e) pairs of lane quarter q with 16 i + 4 q + e
+    // >= rows are a suffix of the pair order; columns past the group drop cb
+    {
+        const int left = rows - 4 * q;                 // valid (i, e) pairs: a prefix of length pv
+        const int pv = left <= 0 ? 0 : min(4 * (left >> 4) + min(left & 15, 4), 4 * NRB);
+        const uint32_t cols = (col_base < G.n ? 0x55555555u : 0u) | (col_base + 16 < G.n ? 0xAAAAAAAAu : 0u);
+        risk[0] &= (pv >= 16 ? ~0u : (1u << (2 * pv)) - 1u) & cols;
+        risk[1] &= (pv >= 32 ? ~0u : (pv <= 16 ? 0u : (1u << (2 * (pv - 16))) - 1u)) & cols;
     }
+    // list the outputs at risk, lane by lane (few lanes hold any); every 64
+    // entries beyond the first 64 are recomputed here (rare)
+    int lrow = 0, lcol = 0, n = 0;
+    bool full = false;             // the first 64 entries are listed
+    uint64_t lanes = __ballot((risk[0] | risk[1]) != 0u);
+    while (lanes) {
+        const int l = __builtin_ctzll(lanes);
+        lanes &= lanes - 1;
+        uint64_t bits = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)risk[0], l) |
+                        (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)risk[1], l) << 32;
+        while (bits) {
+            const int bi = __builtin_ctzll(bits);
+            bits &= bits - 1;
+            const int pair = bi >> 1, cb = bi & 1;     // pair = 4 i + e
+            const int orow = m0 + 16 * (pair >> 2) + 4 * (l >> 4) + (pair & 3);
+            const int ocol = n0 + 32 * wave + 16 * cb + (l & 15);
+            lrow = lane == n ? orow : lrow;
+            lcol = lane == n ? ocol : lcol;
+            if (++n == 64) {
+                if (!full) {
+                    first = FixList{lrow, lcol, 64};
+                    full = true;
+                } else {
+                    store_exact_more(G.a, G.sfa, G.b, G.sfb, G.c, G.m, G.n, G.k, lrow, lcol, 64);
+                }
+                n = 0;
+            }
+        }
+    }
+    if (!full)
+        first = FixList{lrow, lcol, n};
+    else if (n > 0)
+        store_exact_more(G.a, G.sfa, G.b, G.sfb, G.c, G.m, G.n, G.k, lrow, lcol, n);
+    return first;
 }
 
 // One tile's share of this workgroup: pairs [pb, pe).  `w` is the logical
 // workgroup index, [lo, hi) its cost range.
 template <int NRB, int W>
-__device__ __forceinline__ void run_tile(const LaunchArgs &args, uint32_t epoch, const TilePos &p, int pb, int pe, int w,
-                                         int wave, uint8_t *smem)
+__device__ __forceinline__ FixList run_tile(const LaunchArgs &args, const GroupArgs &G, uint32_t epoch,
+                                            const TilePos &p, int pb, int pe, int w, int wave, uint8_t *smem)
 {
-    const GroupArgs &G = args.g[p.g];
     const int m0 = p.rt * G.tile_rows, n0 = p.strip * kTileN;
     const int rows = min(G.tile_rows, G.m - m0);
     f32x4 outer[NRB][2];
@@ -1101,7 +1204,7 @@ __device__ __forceinline__ void run_tile(const LaunchArgs &args, uint32_t epoch,
         segment<NRB, W>(G, args.control + 2, args.sync_spin_limit, m0, n0, wave, smem, sb, se, outer);
         if (pb > 0) {              // a later part of a split tile
             publish_partial<NRB>(args, epoch, w, wave, outer);
-            return;
+            return FixList{0, 0, 0};
         }
         // finalizer: add the other parts of the tile in k order
         bool recompute = false;
@@ -1130,7 +1233,7 @@ __device__ __forceinline__ void run_tile(const LaunchArgs &args, uint32_t epoch,
         ++parts;                   // the recomputed part restarts its sums too
     }
     store_tile<NRB>(G, m0, rows, n0, wave, outer);
-    fix_small_outputs<NRB>(G, m0, rows, n0, wave, parts, outer);
+    return fix_small_outputs<NRB>(G, m0, rows, n0, wave, parts, outer);
 }
 
 template <int W>
@@ -1138,39 +1241,53 @@ __global__ __launch_bounds__(64 * W, 1) void nvfp4_group_gemm_kernel(const Launc
 {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
 
-    // Logical workgroup index: consecutive ranges (which share A rows and B
-    // columns) on the same XCD when workgroups are dealt round-robin to 8 XCDs.
-    const int b = blockIdx.x, nwg = args.num_wg;
-    const int w = (nwg % 8 == 0) ? (b % 8) * (nwg / 8) + b / 8 : b;
+    const int nwg = args.num_wg;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // Two rounds of argument loads before the first operand load: this
+    // block's start record, then (all at once) its first group's fields, its
+    // cost range and the epoch word.  Pinning the values in one asm keeps the
+    // compiler from sinking those loads to their first uses, which would make
+    // them dependent rounds of their own.
+    const WgStart fs = args.first[blockIdx.x];
+    const int w = fs.w;
+    TilePos p = unpack_pos(fs.pos);
+    GroupArgs G = args.g[p.g];
+    int64_t lo = args.cut[w];
+    int64_t hi = args.cut[w + 1];
     // this launch's epoch: one past the last finished launch's (0 marks an
     // unwritten flag); no workgroup changes it before all have started
-    const uint32_t last = (uint32_t)__builtin_amdgcn_readfirstlane(
-        (int)__hip_atomic_load(&args.control[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    uint32_t last = __hip_atomic_load(&args.control[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("" : "+s"(G.a), "+s"(G.b), "+s"(G.sfa), "+s"(G.sfb), "+s"(G.c), "+s"(G.m), "+s"(G.n), "+s"(G.k),
+                 "+s"(G.tile_rows), "+s"(G.npairs), "+s"(G.row_tiles), "+s"(G.cost_full), "+s"(G.cost_last),
+                 "+s"(G.strip_cost), "+s"(G.cost_begin), "+s"(lo), "+s"(hi), "+v"(last));
+    last = (uint32_t)__builtin_amdgcn_readfirstlane((int)last);
     const uint32_t epoch = last + 1u == 0u ? 1u : last + 1u;
-    const int64_t lo = args.cut[w];
-    const int64_t hi = args.cut[w + 1];
 
-    TilePos p = unpack_start(args, args.start[w]);
-    while (p.g < args.ng) {
-        const int npairs = args.g[p.g].npairs;
-        int pb, pe;
-        pairs_in(p, npairs, lo, hi, pb, pe);
-        if (pb >= pe)
-            break;
+    int pb = p.pair, pe = fs.pe;
+    while (pb < pe) {
+        finish_pos(G, p);
+        FixList fix;
         switch (p.nrb) {
-        case 1: run_tile<1, W>(args, epoch, p, pb, pe, w, wave, smem); break;
-        case 2: run_tile<2, W>(args, epoch, p, pb, pe, w, wave, smem); break;
-        case 3: run_tile<3, W>(args, epoch, p, pb, pe, w, wave, smem); break;
-        case 4: run_tile<4, W>(args, epoch, p, pb, pe, w, wave, smem); break;
-        case 5: run_tile<5, W>(args, epoch, p, pb, pe, w, wave, smem); break;
-        case 6: run_tile<6, W>(args, epoch, p, pb, pe, w, wave, smem); break;
-        case 7: run_tile<7, W>(args, epoch, p, pb, pe, w, wave, smem); break;
-        default: run_tile<8, W>(args, epoch, p, pb, pe, w, wave, smem); break;
+        case 1: fix = run_tile<1, W>(args, G, epoch, p, pb, pe, w, wave, smem); break;
+        case 2: fix = run_tile<2, W>(args, G, epoch, p, pb, pe, w, wave, smem); break;
+        case 3: fix = run_tile<3, W>(args, G, epoch, p, pb, pe, w, wave, smem); break;
+        case 4: fix = run_tile<4, W>(args, G, epoch, p, pb, pe, w, wave, smem); break;
+        case 5: fix = run_tile<5, W>(args, G, epoch, p, pb, pe, w, wave, smem); break;
+        case 6: fix = run_tile<6, W>(args, G, epoch, p, pb, pe, w, wave, smem); break;
+        case 7: fix = run_tile<7, W>(args, G, epoch, p, pb, pe, w, wave, smem); break;
+        default: fix = run_tile<8, W>(args, G, epoch, p, pb, pe, w, wave, smem); break;
         }
-        if (pe < npairs)
+        // the tile's outputs at risk of exceeding the tolerance, recomputed
+        // exactly over its stored values (one copy for every tile height)
+        if (fix.n > 0)
+            store_exact<false>(G.a, G.sfa, G.b, G.sfb, G.c, G.m, G.n, G.k, fix.lrow, fix.lcol, fix.n);
+        if (pe < G.npairs)
             break;                 // the range ends inside this tile
         p = next_tile(args.g, args.ng, args.total_cost, p);
+        if (p.g >= args.ng)
+            break;
+        G = args.g[p.g];
+        pairs_in(p, G.npairs, lo, hi, pb, pe);
     }
     // The last workgroup to finish resets the count and records the epoch
     // for the next launch on this workspace (ordered after this one by the
@@ -1409,9 +1526,37 @@ struct CutCache {
     int nwg = -1, ng = 0;
     int32_t mnk[kMaxGroupsPerLaunch][3];
     int64_t cut[kMaxWorkgroups + 1];
-    uint64_t start[kMaxWorkgroups];
+    WgStart first[kMaxWorkgroups];
 };
 thread_local CutCache g_cut_cache;
+
+// Logical workgroup of block b (see WgStart).
+inline int logical_wg(int b, int nwg)
+{
+    return nwg % 8 == 0 ? (b % 8) * (nwg / 8) + b / 8 : b;
+}
+
+// The start records of a launch whose cuts are set.
+void fill_starts(LaunchArgs &a, int nwg)
+{
+    for (int b = 0; b < nwg; ++b) {
+        const int w = logical_wg(b, nwg);
+        TilePos p = locate(a, a.cut[w]);
+        WgStart &f = a.first[b];
+        f.w = w;
+        f.pe = 0;
+        f.pos = 0;                 // no tile: group 0, no pairs
+        if (p.g < a.ng) {
+            int pb, pe;
+            pairs_in(p, a.g[p.g].npairs, a.cut[w], a.cut[w + 1], pb, pe);
+            if (pb < pe) {
+                p.pair = pb;
+                f.pos = pack_start(p, a.ng);
+                f.pe = pe;
+            }
+        }
+    }
+}
 
 void plan_cuts(LaunchArgs &a, int nwg)
 {
@@ -1421,7 +1566,7 @@ void plan_cuts(LaunchArgs &a, int nwg)
         same = cc.mnk[i][0] == a.g[i].m && cc.mnk[i][1] == a.g[i].n && cc.mnk[i][2] == a.g[i].k;
     if (same) {
         memcpy(a.cut, cc.cut, sizeof(int64_t) * (nwg + 1));
-        memcpy(a.start, cc.start, sizeof(uint64_t) * nwg);
+        memcpy(a.first, cc.first, sizeof(WgStart) * nwg);
         return;
     }
     std::vector<PlanTile> tiles;
@@ -1446,8 +1591,7 @@ void plan_cuts(LaunchArgs &a, int nwg)
             lo = mid;
     }
     greedy_cuts(tiles, nwg, a.total_cost, hi, a.cut);
-    for (int w = 0; w < nwg; ++w)
-        a.start[w] = pack_start(locate(a, a.cut[w]), a.ng);
+    fill_starts(a, nwg);
     cc.nwg = nwg;
     cc.ng = a.ng;
     for (int i = 0; i < a.ng; ++i) {
@@ -1456,7 +1600,7 @@ void plan_cuts(LaunchArgs &a, int nwg)
         cc.mnk[i][2] = a.g[i].k;
     }
     memcpy(cc.cut, a.cut, sizeof(int64_t) * (nwg + 1));
-    memcpy(cc.start, a.start, sizeof(uint64_t) * nwg);
+    memcpy(cc.first, a.first, sizeof(WgStart) * nwg);
 }
 
 // Library-owned workspace for one stream: partial-sum slots, their flags,
@@ -1671,16 +1815,20 @@ extern "C" int nvfp4_plan(const nvfp4_group_t *groups, int ng, int num_workgroup
         launch_first = next;
         const int nwg = grid_for(args, num_workgroups);
         plan_cuts(args, nwg);
+        // the kernel's walk (its start records, then pairs_in per tile),
+        // listed in logical workgroup order
+        int block_of[kMaxWorkgroups];
+        for (int b = 0; b < nwg; ++b)
+            block_of[args.first[b].w] = b;
         for (int w = 0; w < nwg; ++w) {
+            const WgStart &fs = args.first[block_of[w]];
             const int64_t lo = args.cut[w];
             const int64_t hi = args.cut[w + 1];
-            TilePos p = unpack_start(args, args.start[w]);
-            while (p.g < args.ng) {
+            TilePos p = unpack_pos(fs.pos);
+            int pb = p.pair, pe = fs.pe;
+            while (pb < pe) {
                 const GroupArgs &G = args.g[p.g];
-                int pb, pe;
-                pairs_in(p, G.npairs, lo, hi, pb, pe);
-                if (pb >= pe)
-                    break;
+                finish_pos(G, p);
                 if (segs != nullptr && count < cap) {
                     int32_t *o = segs + 8 * count;
                     const int m0 = p.rt * G.tile_rows;
@@ -1697,6 +1845,9 @@ extern "C" int nvfp4_plan(const nvfp4_group_t *groups, int ng, int num_workgroup
                 if (pe < G.npairs)
                     break;
                 p = next_tile(args.g, args.ng, args.total_cost, p);
+                if (p.g >= args.ng)
+                    break;
+                pairs_in(p, args.g[p.g].npairs, lo, hi, pb, pe);
             }
         }
     }

@@ -184,6 +184,48 @@ def test_config1_recomputed_parts_full():
             os.environ["NVFP4_SPIN_LIMIT"] = old
 
 
+# Outputs that cancel exactly (workloads.cancelling): their fp32 sums carry
+# rounding errors near the absolute tolerance, so they are recomputed
+# exactly and must come out as zero.  Scale exponents -8..3 and K = 8192
+# put the tile's typical output near 10^4; the small scales make the
+# partial sums inexact in fp32 (with exponents >= 0 every sum here would be
+# a multiple of 2^-8 below 2^16, exact in fp32, and cancel exactly anyway).
+CANCEL_K = 8192
+CANCEL_E = (-8, 3)
+
+
+def _cancel_cols(per_slice, n):
+    """`per_slice` columns in every 32-column slice (one wave's columns)."""
+    return [s + (7 * i) % 32 for s in range(0, n, 32) for i in range(per_slice)]
+
+
+def _check_cancelling(g, rows, cols, label):
+    got = check_full([g], label)[0].reshape(g.m, g.n).view(np.float16).astype(np.float64)
+    zeros = got[np.ix_(rows, cols)]
+    assert np.all(zeros == 0.0), "%s: %d of %d cancelling outputs are not zero, largest %g" % (
+        label, int((zeros != 0).sum()), zeros.size, float(np.abs(zeros).max()))
+
+
+@pytest.mark.parametrize("per_slice", [1, 2, 3, 5, 8, 9, 17])
+def test_cancelling_outputs_per_wave(per_slice):
+    """One row and `per_slice` columns per wave whose outputs are exactly
+    zero: every batch width of the exact recomputation (1, 2, up to 4, up to
+    8 outputs, and more than one batch)."""
+    m, n = 72, 512
+    rows, cols = [5], _cancel_cols(per_slice, n)
+    g = workloads.cancelling(m, n, CANCEL_K, rows, cols, CANCEL_E, seed=per_slice)
+    _check_cancelling(g, rows, cols, "cancelling, %d per wave" % per_slice)
+
+
+def test_cancelling_outputs_beyond_one_list():
+    """40 cancelling rows and every column symmetric: more than 64 outputs
+    of one wave to recompute, so the later lists take the out-of-line copy."""
+    m, n = 72, 256
+    rows, cols = list(range(8, 48)), list(range(n))
+    g = workloads.cancelling(m, n, CANCEL_K, rows, cols, CANCEL_E, seed=3)
+    _check_cancelling(g, rows, cols, "cancelling, 40 rows x all columns")
+
+
 def test_handoff_timeouts_are_counted():
     """Forcing the waves' A hand-off waits to give up at once
     (NVFP4_SYNC_SPIN_LIMIT=0; the kernel still exits normally, only its sums

@@ -29,7 +29,7 @@ from typing import List, Sequence, Tuple
 import numpy as np
 
 __all__ = ["Group", "Workload", "CONFIGS", "make_workload", "encode_scale_e4m3fn",
-           "generate", "config_flops", "config_bytes"]
+           "generate", "cancelling", "config_flops", "config_bytes"]
 
 
 @dataclass(frozen=True)
@@ -116,6 +116,31 @@ def generate(w: Workload) -> List[Group]:
         mb = rng.integers(0, 8, size=(n, k // 16))
         groups.append(Group(m, n, k, a, b, encode_scale_e4m3fn(ea, ma), encode_scale_e4m3fn(eb, mb)))
     return groups
+
+
+def cancelling(m: int, n: int, k: int, rows, cols, e_range=(0, 3), seed: int = 0) -> Group:
+    """One group whose outputs (r, c) for r in ``rows`` and c in ``cols`` are
+    exactly zero while the rest are random (drawn as in ``generate``).
+
+    For each listed row of A the second half of K repeats the first half
+    with every code's sign bit flipped (byte XOR 0x88) and the same scales;
+    for each listed column of B the second half repeats the first half
+    unchanged.  The two halves of such an output's sum are then equal and
+    opposite, whatever the values: large partial sums that cancel exactly.
+    K must be a multiple of 32.
+    """
+    if k % 32:
+        raise ValueError("K must be a multiple of 32")
+    g = generate(make_workload([(m, n, k)], e_range, seed))[0]
+    h, hs = k // 4, k // 32            # half of K in code bytes and in scale bytes
+    a, b, sfa, sfb = g.a.copy(), g.b.copy(), g.sfa.copy(), g.sfb.copy()
+    for r in rows:
+        a[r, h:] = a[r, :h] ^ np.uint8(0x88)
+        sfa[r, hs:] = sfa[r, :hs]
+    for c in cols:
+        b[c, h:] = b[c, :h]
+        sfb[c, hs:] = sfb[c, :hs]
+    return Group(m, n, k, a, b, sfa, sfb)
 
 
 def config_flops(shapes) -> int:
