@@ -1034,12 +1034,16 @@ __device__ __forceinline__ void store_exact(const uint8_t *a, const uint8_t *sfa
                 acc += sum(b0, g);
             }
         } else {
+            // every load issued is summed: a load left in flight at the end
+            // would make later code wait for all memory operations
             load(b0, 0);
             for (int g = 0; g < groups; g += 2) {
-                load(b1, g + 1);
+                if (g + 1 < groups)
+                    load(b1, g + 1);
                 acc += sum(b0, g);
                 if (g + 1 < groups) {
-                    load(b0, g + 2);
+                    if (g + 2 < groups)
+                        load(b0, g + 2);
                     acc += sum(b1, g + 1);
                 }
             }
