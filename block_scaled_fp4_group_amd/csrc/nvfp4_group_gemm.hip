@@ -1306,6 +1306,150 @@ __global__ __launch_bounds__(64 * W, 1) void nvfp4_group_gemm_kernel(const Launc
     }
 }
 
+// ---------------------------------------------------------- direct path --
+// Launches too small to fill the chip (config 0: two 256-k tiles) are bound
+// by latency: the persistent kernel's fill, hand-offs and epilogue cost
+// more than their MFMAs.  Here each wave owns one task of up to 16, 32 or
+// 64 rows (the fewest that keep the task table within kDirectMaxTasks
+// workgroups, so tiny launches spread over more waves) by 32 columns and
+// runs it alone: its operand codes and scales are loaded
+// straight into registers (every load of the whole K at once), decoded as
+// in the persistent kernel, summed by the same MFMA chain with the same
+// 512-k fold, stored by the same epilogue and checked by the same fix-up.
+// Four waves share a workgroup (128 columns) but nothing else.
+constexpr int kDirectWaves = 4;
+constexpr int kDirectRowBlocks = 4;
+constexpr int kDirectRows = 16 * kDirectRowBlocks;
+constexpr int kDirectCols = 32 * kDirectWaves;
+constexpr int kDirectMaxK = 4 * kStageK;       // four 128-k chunks in registers
+constexpr int kDirectMaxTasks = 256;
+constexpr int64_t kDirectMaxUnits = 64;        // (tile, pair) units of the persistent schedule
+
+struct DirectTask {
+    int32_t g, m0, n0, pad;
+};
+
+struct DirectArgs {
+    GroupArgs g[kMaxGroupsPerLaunch];
+    int32_t ntasks;
+    int32_t task_rows;   // 16, 32 or 64
+    int32_t pad_[2];
+    DirectTask task[kDirectMaxTasks];
+};
+
+// One task: rows [m0, m0 + rows) (NRB blocks of 16) and columns [n0 + 32
+// wave, + 32) of group G, in the persistent kernel's register layout
+// (lane (r, q) holds outer[i][cb][e] = C[m0 + 16 i + 4 q + e][n0 + 32 wave
+// + 16 cb + r]) and the same k order within each 128-k chunk (lane q takes
+// k = 32 q + [0, 32), eight of them per MFMA step).
+template <int NRB>
+__device__ __forceinline__ FixList direct_task(const GroupArgs &G, int m0, int rows, int n0, int wave)
+{
+    const int lane = lane_id();
+    const int r = lane & 15, q = lane >> 4;
+    const int M = G.m, N = G.n, K = G.k;
+    const uint32_t row_bytes = (uint32_t)K >> 1, row_sc = (uint32_t)K >> 4;
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void *)G.a, 0, M * (int)row_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc((void *)G.sfa, 0, M * (int)row_sc, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void *)G.b, 0, N * (int)row_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc((void *)G.sfb, 0, N * (int)row_sc, 0x00020000);
+    uint32_t a_off[NRB], sa_off[NRB], b_off[2], sb_off[2];
+#pragma unroll
+    for (int i = 0; i < NRB; ++i) {
+        const uint32_t row = (uint32_t)min(m0 + 16 * i + r, M - 1);
+        a_off[i] = row * row_bytes + 16u * q;
+        sa_off[i] = row * row_sc + 2u * q;
+    }
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+        const uint32_t col = (uint32_t)min(n0 + 32 * wave + 16 * cb + r, N - 1);
+        b_off[cb] = col * row_bytes + 16u * q;
+        sb_off[cb] = col * row_sc + 2u * q;
+    }
+    const int nch = (K + kStageK - 1) / kStageK;    // <= 4
+    // every chunk's loads first; chunks past K are not loaded
+    u32x4 ac[4][NRB], bc[4][2];
+    uint32_t sa[4][NRB], sb[4][2];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        if (c < nch) {
+            const uint32_t kb = (uint32_t)c * (kStageK / 2), ks = (uint32_t)c * (kStageK / 16);
+#pragma unroll
+            for (int i = 0; i < NRB; ++i) {
+                ac[c][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, a_off[i] + kb, 0, 0));
+                sa[c][i] = __builtin_amdgcn_raw_buffer_load_b16(rsa, sa_off[i] + ks, 0, 0);
+            }
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
+                bc[c][cb] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, b_off[cb] + kb, 0, 0));
+                sb[c][cb] = __builtin_amdgcn_raw_buffer_load_b16(rsb, sb_off[cb] + ks, 0, 0);
+            }
+        }
+    }
+    f32x4 outer[NRB][2];
+#pragma unroll
+    for (int i = 0; i < NRB; ++i)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+            outer[i][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // K <= 512: one MFMA chain over all chunks, folded once (the persistent
+    // kernel folds every 512 k, so the sums round the same way)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        if (c < nch) {
+            // lanes whose 32 k lie past K get zero scales (K % 64 == 0)
+            const bool valid = c * kStageK + 32 * q < K;
+            f16x2 sca[NRB], scb[2];
+#pragma unroll
+            for (int i = 0; i < NRB; ++i)
+                sca[i] = scales2(valid ? sa[c][i] : 0u);
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+                scb[cb] = scales2(valid ? sb[c][cb] : 0u);
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) {
+                f16x8 bf[2];
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb)
+                    bf[cb] = decode8(bc[c][cb][s2], bcast(scb[cb][s2 >> 1]));
+#pragma unroll
+                for (int i = 0; i < NRB; ++i) {
+                    const f16x8 af = decode8(ac[c][i][s2], bcast(sca[i][s2 >> 1]));
+#pragma unroll
+                    for (int cb = 0; cb < 2; ++cb)
+                        outer[i][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[cb], outer[i][cb], 0, 0, 0);
+                }
+            }
+        }
+    }
+    store_tile<NRB>(G, m0, rows, n0, wave, outer);
+    return fix_small_outputs<NRB>(G, m0, rows, n0, wave, 0, outer);
+}
+
+__global__ __launch_bounds__(64 * kDirectWaves) void nvfp4_direct_kernel(const DirectArgs args)
+{
+    // two rounds of argument loads: the task, then its group's fields (all
+    // at once, pinned so the compiler cannot sink them to their uses)
+    const DirectTask t = args.task[blockIdx.x];
+    GroupArgs G = args.g[t.g];
+    int task_rows = args.task_rows;
+    asm volatile("" : "+s"(G.a), "+s"(G.b), "+s"(G.sfa), "+s"(G.sfb), "+s"(G.c), "+s"(G.m), "+s"(G.n), "+s"(G.k),
+                 "+s"(task_rows));
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (t.n0 + 32 * wave >= G.n)
+        return;                    // this wave's columns lie past the group (no barrier follows)
+    const int rows = min(task_rows, G.m - t.m0);
+    FixList fix;
+    switch ((rows + 15) >> 4) {
+    case 1: fix = direct_task<1>(G, t.m0, rows, t.n0, wave); break;
+    case 2: fix = direct_task<2>(G, t.m0, rows, t.n0, wave); break;
+    case 3: fix = direct_task<3>(G, t.m0, rows, t.n0, wave); break;
+    default: fix = direct_task<4>(G, t.m0, rows, t.n0, wave); break;
+    }
+    if (fix.n > 0)
+        store_exact<false>(G.a, G.sfa, G.b, G.sfb, G.c, G.m, G.n, G.k, fix.lrow, fix.lcol, fix.n);
+}
+
 // ------------------------------------------------------------------ host --
 
 thread_local char g_err[512];
@@ -1739,8 +1883,51 @@ int static_scratch(int device, uint8_t *&out)
 
 // Every launch of one call: the stream's allocated workspace, or (use_static)
 // the device's static one.
+// Path of a launch: NVFP4_PATH=main or =direct forces one (direct only
+// where its argument table fits); by default the direct path takes
+// launches whose every K is at most kDirectMaxK and whose persistent
+// schedule would have at most kDirectMaxUnits (tile, pair) units.
+int path_override()
+{
+    const char *e = getenv("NVFP4_PATH");
+    if (e == nullptr)
+        return 0;
+    if (strcmp(e, "main") == 0)
+        return 1;
+    if (strcmp(e, "direct") == 0)
+        return 2;
+    return 0;
+}
+
+// The direct path's task table for a packed launch; false if it does not
+// fit (some K above kDirectMaxK, or more than kDirectMaxTasks tasks).
+bool direct_tasks(const LaunchArgs &args, DirectArgs &d)
+{
+    for (int gi = 0; gi < args.ng; ++gi)
+        if (args.g[gi].k > kDirectMaxK)
+            return false;
+    for (int rows = 16; rows <= kDirectRows; rows *= 2) {
+        int64_t count = 0;
+        for (int gi = 0; gi < args.ng; ++gi)
+            count += (int64_t)ceil_div(args.g[gi].m, rows) * ceil_div(args.g[gi].n, kDirectCols);
+        if (count > kDirectMaxTasks)
+            continue;
+        int n = 0;
+        for (int gi = 0; gi < args.ng; ++gi)
+            for (int m0 = 0; m0 < args.g[gi].m; m0 += rows)
+                for (int n0 = 0; n0 < args.g[gi].n; n0 += kDirectCols)
+                    d.task[n++] = DirectTask{gi, m0, n0, 0};
+        memcpy(d.g, args.g, sizeof d.g);
+        d.ntasks = n;
+        d.task_rows = rows;
+        return true;
+    }
+    return false;
+}
+
 int launch_all(const nvfp4_group_t *groups, int ng, hipStream_t st, bool use_static)
 {
+    const int path = path_override();
     int device = 0, units = 0;
     LaunchArgs args;
     int next = 0;
@@ -1748,6 +1935,16 @@ int launch_all(const nvfp4_group_t *groups, int ng, hipStream_t st, bool use_sta
     while (next < ng) {
         if (pack_launch(groups, ng, next, args) == 0)
             break;
+        if (path != 1 && (path == 2 || total_pairs(args) <= kDirectMaxUnits)) {
+            DirectArgs d;
+            if (direct_tasks(args, d)) {
+                hipLaunchKernelGGL(nvfp4_direct_kernel, dim3((unsigned)d.ntasks), dim3(64 * kDirectWaves), 0, st, d);
+                const hipError_t e = hipGetLastError();
+                if (e != hipSuccess)
+                    return fail(NVFP4_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+                continue;
+            }
+        }
         if (!queried) {
             const int rc2 = device_units(device, units);
             if (rc2 != NVFP4_OK)

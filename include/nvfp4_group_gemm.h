@@ -98,6 +98,15 @@ typedef struct nvfp4_group {
  * 256) workgroups, whose work ranges the host balances with a timing model
  * of the kernel (tens of microseconds); the last result is reused, per host
  * thread, while the groups' sizes stay the same.
+ * Tiny launches: a launch (up to 32 groups) whose every k is at most 512
+ * and whose work is at most 64 units of 128 or fewer rows x 256 columns x
+ * 256 k goes to a direct kernel instead: one wave per 16, 32 or 64 rows x 32
+ * columns, operands loaded straight into registers, no split tiles, hence
+ * no workspace (such a call may be captured on any stream).  Its sums round
+ * exactly as the persistent kernel's for k <= 256.  The environment
+ * variable NVFP4_PATH (read at each call) forces a path: "main" (the
+ * persistent kernel) or "direct" (wherever every k is at most 512 and at
+ * most 256 workgroups of 4 waves suffice).
  */
 int nvfp4_group_gemm(const nvfp4_group_t *groups, int ng, void *stream);
 
@@ -125,8 +134,9 @@ int nvfp4_group_gemm_noalloc(const nvfp4_group_t *groups, int ng, void *stream);
 int nvfp4_validate(const nvfp4_group_t *groups, int ng);
 
 /*
- * Host-only view of the work decomposition a launch on a device with
- * `num_workgroups` compute units would use.  Writes up to `cap` segment
+ * Host-only view of the work decomposition the persistent kernel would use
+ * for a launch on a device with `num_workgroups` compute units (tiny
+ * launches take the direct kernel instead; see nvfp4_group_gemm).  Writes up to `cap` segment
  * records of eight int32 each and returns the total number of segments
  * (which may exceed cap), or a negative NVFP4 code negated on invalid input.
  *

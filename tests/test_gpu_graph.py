@@ -4,7 +4,9 @@ every replay gets a fresh epoch.  Consecutive replays run on new inputs
 (uploaded between them, with no other library call); every output of every
 replay is compared with the oracle on those inputs, and with an eager call
 bit for bit.  The allocation-free entry point is captured the same way on a
-stream that has never been used, and the regular one refuses such a stream."""
+stream that has never been used, and the regular one refuses such a stream
+(it needs its workspace) unless the launch is tiny enough for the direct
+path, which needs none."""
 import numpy as np
 import pytest
 
@@ -21,8 +23,11 @@ SHAPES = [(200, 512, 2048), (72, 1024, 4096), (130, 256, 1536)]   # every tile s
 REPLAYS = 4
 
 
-def _fresh(seed):
-    return workloads.generate(workloads.make_workload(SHAPES, (-4, 2), seed, "graph"))
+TINY = [(64, 128, 256), (128, 256, 256)]   # config 0's shapes: the direct path
+
+
+def _fresh(seed, shapes=SHAPES):
+    return workloads.generate(workloads.make_workload(shapes, (-4, 2), seed, "graph"))
 
 
 def _load(args, groups):
@@ -33,19 +38,19 @@ def _load(args, groups):
     torch.cuda.synchronize()
 
 
-def _replay_and_check(g, args, descs, stream, eager_fn):
+def _replay_and_check(g, args, descs, stream, eager_fn, shapes=SHAPES):
     import torch
     import block_scaled_fp4_group_amd as nv
     replayed = []
     for rep in range(REPLAYS):
         log("graph replay %d" % rep)
-        _load(args, _fresh(100 + rep))
+        _load(args, _fresh(100 + rep, shapes))
         g.replay()
         torch.cuda.synchronize()
         replayed.append([x[4].cpu().numpy().view(np.uint16).copy() for x in args])
     assert nv.stream_errors(stream.cuda_stream) == 0
     for rep in range(REPLAYS):
-        groups = _fresh(100 + rep)
+        groups = _fresh(100 + rep, shapes)
         r16, r64 = oracle.group_gemm(groups)
         for i, (got, rb, rx) in enumerate(zip(replayed[rep], r16, r64)):
             res = compare_fp16(got, rb, rx)
@@ -109,3 +114,20 @@ def test_regular_entry_refuses_capture_without_workspace():
             nv.group_gemm_raw(descs, s.cuda_stream)
     assert err.value.code == nv.NVFP4_EUNSUPPORTED
     torch.cuda.synchronize()
+
+
+def test_direct_path_capture_on_a_new_stream():
+    import torch
+    import block_scaled_fp4_group_amd as nv
+    args = device_args(_fresh(14, TINY))
+    descs = [nv._descriptor(*a) for a in args]
+    s = torch.cuda.Stream()                         # never used before: no workspace, none needed
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        nv.group_gemm_raw(descs, s.cuda_stream)
+    torch.cuda.synchronize()
+
+    def eager():
+        with torch.cuda.stream(s):
+            nv.group_gemm_raw(descs, s.cuda_stream)
+    _replay_and_check(g, args, descs, s, eager, TINY)

@@ -184,6 +184,69 @@ def test_config1_recomputed_parts_full():
             os.environ["NVFP4_SPIN_LIMIT"] = old
 
 
+# The direct path (tiny launches: every K <= 512 and few (tile, pair)
+# units) against the oracle, and against the persistent path, which can be
+# forced with NVFP4_PATH=main (and the direct path with =direct).
+DIRECT_SHAPES = [(1, 17, 64), (65, 130, 320), (130, 64, 512), (16, 1, 128), (63, 65, 256), (64, 128, 256),
+                 (128, 256, 256), (77, 300, 448), (200, 129, 192)]
+
+
+class forced_path:
+    def __init__(self, path):
+        self.path = path
+
+    def __enter__(self):
+        import os
+        self.old = os.environ.get("NVFP4_PATH")
+        if self.path is None:
+            os.environ.pop("NVFP4_PATH", None)
+        else:
+            os.environ["NVFP4_PATH"] = self.path
+
+    def __exit__(self, *exc):
+        import os
+        if self.old is None:
+            os.environ.pop("NVFP4_PATH", None)
+        else:
+            os.environ["NVFP4_PATH"] = self.old
+
+
+@pytest.mark.parametrize("path", ["main", "direct"])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_small_shapes_both_paths(seed, path):
+    """Ragged small groups (M, N not multiples of 16, 32, 64 or 128; K from
+    64 to 512, not all multiples of 128) in one launch, on each path."""
+    groups = workloads.generate(workloads.make_workload(DIRECT_SHAPES, (-8, 4), 40 + seed, "direct"))
+    with forced_path(path):
+        check_full(groups, "small shapes, %s path, seed %d" % (path, seed))
+
+
+def test_direct_path_matches_persistent_bitwise():
+    """With K <= 256 (one stage pair, so no tile is split) both paths sum
+    every output in the same order with the same roundings: bit for bit."""
+    shapes = [(s[0], s[1], min(s[2], 256)) for s in DIRECT_SHAPES]
+    groups = workloads.generate(workloads.make_workload(shapes, (-8, 4), 44, "direct_vs_main"))
+    with forced_path("main"):
+        a = check_full(groups, "persistent path, K <= 256")
+    with forced_path("direct"):
+        b = check_full(groups, "direct path, K <= 256")
+    for i, (x, y) in enumerate(zip(a, b)):
+        nd = int((x != y).sum())
+        assert nd == 0, "group %d: %d outputs differ between the paths" % (i, nd)
+
+
+def test_direct_path_cancelling_outputs():
+    """The direct path's fix-up: outputs that cancel exactly at K = 512
+    (scale exponents up to 4 put the typical output near 10^4) come out zero."""
+    m, n = 64, 256
+    rows, cols = [3, 40], [s + (7 * i) % 32 for s in range(0, n, 32) for i in range(5)]
+    g = workloads.cancelling(m, n, 512, rows, cols, (-8, 4), seed=9)
+    with forced_path("direct"):
+        got = check_full([g], "direct path, cancelling")[0].reshape(m, n).view(np.float16).astype(np.float64)
+    zeros = got[np.ix_(rows, cols)]
+    assert np.all(zeros == 0.0), "%d cancelling outputs are not zero" % int((zeros != 0).sum())
+
+
 # Outputs that cancel exactly (workloads.cancelling): their fp32 sums carry
 # rounding errors near the absolute tolerance, so they are recomputed
 # exactly and must come out as zero.  Scale exponents -8..3 and K = 8192
