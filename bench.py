@@ -10,6 +10,9 @@ in HBM, and prints one JSON line with:
 - the same figures for every one of the five workloads (`config.per_workload`),
   each also as a fraction of the dense f16 MFMA peak the kernel computes on;
 - the host cost of one call and of one graph replay of the small workload;
+- for the four large workloads, the kernel time with B's scales in the
+  optional window-major layout (`sfb_window_major_us`; the headline figures
+  use the plain row-major scales the inputs come in);
 - the CPU oracle timed on a bounded sample as a baseline.
 
 Cold-cache protocol: each step runs on one of R input/output replicas in
@@ -133,11 +136,13 @@ def launches_per_step(w):
     return max(1, -(-n // 32))
 
 
-def time_workload(w, steps, warmup, warm_cache):
+def time_workload(w, steps, warmup, warm_cache, sfb_swizzled=False):
     """Protocol of one workload (the trace summary relies on its launch
     order): `warmup` untimed calls, `steps` timed calls bracketed by one
     event pair on the launch stream (and host wall time), then `steps`
-    single calls each bracketed by its own events."""
+    single calls each bracketed by its own events.  With sfb_swizzled, B's
+    scales are first copied into the window-major layout (nvfp4_swizzle_scales,
+    outside the timed calls) and passed with NVFP4_SFB_SWIZZLED."""
     import torch
     import block_scaled_fp4_group_amd as nv
     dev = torch.device("cuda:0")
@@ -146,7 +151,11 @@ def time_workload(w, steps, warmup, warm_cache):
     flops = workloads.config_flops(w.shapes)
     reps = 1 if warm_cache else max(2, -(-2 * MALL_BYTES // max(1, nbytes)) + 1)
     replicas = build_replicas(groups, reps, dev)
-    descs = [[nv._descriptor(*g) for g in rep] for rep in replicas]
+    if sfb_swizzled:
+        replicas = [[(a, b, sa, nv.swizzle_scales(sb), c) for (a, b, sa, sb, c) in rep] for rep in replicas]
+        descs = [[nv._descriptor(*g, sfb_swizzled=True) for g in rep] for rep in replicas]
+    else:
+        descs = [[nv._descriptor(*g) for g in rep] for rep in replicas]
     stream = torch.cuda.current_stream()
     sid = stream.cuda_stream
     for i in range(warmup):
@@ -298,15 +307,17 @@ def trace_protocol(steps, warmup, headline_only, config=HEADLINE):
     regions marked."""
     blocks = []
 
-    def add(w, st, wu):
+    def add(w, st, wu, tag=""):
         n = launches_per_step(w)
-        blocks.append((w.name + " warmup", wu * n, False))
-        blocks.append((w.name + " timed", st * n, True))
-        blocks.append((w.name + " single", st * n, False))
+        blocks.append((w.name + tag + " warmup", wu * n, False))
+        blocks.append((w.name + tag + " timed", st * n, True))
+        blocks.append((w.name + tag + " single", st * n, False))
     add(workloads.CONFIGS[config], steps, warmup)
     if not headline_only:
-        for w in workloads.CONFIGS:
+        for i, w in enumerate(workloads.CONFIGS):
             add(w, PER_WORKLOAD_STEPS, PER_WORKLOAD_WARMUP)
+            if i > 0:
+                add(w, PER_WORKLOAD_STEPS, PER_WORKLOAD_WARMUP, " (window-major sfb)")
     return blocks
 
 
@@ -317,7 +328,8 @@ def summarize_trace(path, steps, warmup, headline_only, config=HEADLINE):
     rows = []
     with open(path) as f:
         for r in csv.DictReader(f):
-            if "nvfp4_group_gemm_kernel" in r.get("Kernel_Name", ""):
+            name = r.get("Kernel_Name", "")
+            if "nvfp4_group_gemm_kernel" in name or "nvfp4_direct_kernel" in name:
                 rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
     rows.sort()
     durs = [(e - s) / 1e3 for s, e in rows]
@@ -327,7 +339,7 @@ def summarize_trace(path, steps, warmup, headline_only, config=HEADLINE):
         seg = durs[i:i + n]
         i += n
         if timed and seg:
-            print("%-48s launches %3d  mean %8.2f us  median %8.2f us  min %8.2f us"
+            print("%-66s launches %3d  mean %8.2f us  median %8.2f us  min %8.2f us"
                   % (label, len(seg), float(np.mean(seg)), float(np.median(seg)), float(np.min(seg))))
     print("remaining dispatches (host-cost calls, graph replays): %d" % max(0, len(durs) - i))
 
@@ -367,11 +379,20 @@ def main():
     tflops = r["flops"] / (r["wall_ms"] * 1e-3) / 1e12     # whole-job rate over the timed steps
     per_workload = []
     if not args.headline_only:
-        for wc in workloads.CONFIGS:
+        for i, wc in enumerate(workloads.CONFIGS):
             rc = time_workload(wc, PER_WORKLOAD_STEPS, PER_WORKLOAD_WARMUP, args.warm_cache)
             per_workload.append(workload_entry(wc, rc, args.warm_cache))
             del rc
             torch.cuda.empty_cache()
+            if i > 0:
+                # the optional window-major layout of B's scales (a one-time
+                # copy of a weight operand's scales), timed right after the
+                # plain layout the inputs come in, which the headline uses
+                rc = time_workload(wc, PER_WORKLOAD_STEPS, PER_WORKLOAD_WARMUP, args.warm_cache,
+                                   sfb_swizzled=True)
+                per_workload[-1]["sfb_window_major_us"] = round(rc["ev_ms_mean"] * 1e3, 2)
+                del rc
+                torch.cuda.empty_cache()
         host_us, graph_us = host_and_graph_cost(workloads.CONFIGS[0])
         per_workload[0]["host_us_per_call"] = host_us
         per_workload[0]["graph_replay_us"] = graph_us

@@ -11,12 +11,13 @@ import ctypes
 import os
 from typing import Iterable, List, Sequence, Tuple
 
-__all__ = ["NVFP4_OK", "NVFP4_EINVAL", "NVFP4_EUNSUPPORTED", "NVFP4_EHIP", "Nvfp4Error",
+__all__ = ["NVFP4_OK", "NVFP4_EINVAL", "NVFP4_EUNSUPPORTED", "NVFP4_EHIP", "NVFP4_SFB_SWIZZLED", "Nvfp4Error",
            "Nvfp4Group", "lib", "library_path", "group_gemm", "group_gemm_raw", "group_gemm_noalloc_raw",
-           "validate",
+           "validate", "swizzled_scale_bytes", "swizzle_scales",
            "plan", "release_workspace", "stream_errors", "tile_rows", "tile_cols", "make_group"]
 
 NVFP4_OK, NVFP4_EINVAL, NVFP4_EUNSUPPORTED, NVFP4_EHIP = 0, 1, 2, 3
+NVFP4_SFB_SWIZZLED = 1
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG_DIR, "libnvfp4gg.so")
@@ -33,7 +34,7 @@ class Nvfp4Group(ctypes.Structure):
     """Mirror of nvfp4_group_t."""
     _fields_ = [("a", ctypes.c_void_p), ("b", ctypes.c_void_p), ("sfa", ctypes.c_void_p),
                 ("sfb", ctypes.c_void_p), ("c", ctypes.c_void_p), ("m", ctypes.c_int32),
-                ("n", ctypes.c_int32), ("k", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("n", ctypes.c_int32), ("k", ctypes.c_int32), ("flags", ctypes.c_int32)]
 
 
 def lib():
@@ -57,6 +58,11 @@ def lib():
         L.nvfp4_release_workspace.argtypes = [ctypes.c_void_p]
         L.nvfp4_stream_errors.restype = ctypes.c_int
         L.nvfp4_stream_errors.argtypes = [ctypes.c_void_p]
+        L.nvfp4_swizzled_scale_bytes.restype = ctypes.c_int64
+        L.nvfp4_swizzled_scale_bytes.argtypes = [ctypes.c_int, ctypes.c_int]
+        L.nvfp4_swizzle_scales.restype = ctypes.c_int
+        L.nvfp4_swizzle_scales.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_void_p]
         L.nvfp4_tile_rows.restype = ctypes.c_int
         L.nvfp4_tile_cols.restype = ctypes.c_int
         L.nvfp4_last_error.restype = ctypes.c_char_p
@@ -68,9 +74,9 @@ def _last_error() -> str:
     return lib().nvfp4_last_error().decode(errors="replace")
 
 
-def make_group(a=0, b=0, sfa=0, sfb=0, c=0, m=0, n=0, k=0, reserved=0) -> Nvfp4Group:
+def make_group(a=0, b=0, sfa=0, sfb=0, c=0, m=0, n=0, k=0, flags=0) -> Nvfp4Group:
     """A group descriptor from raw device addresses (ints) and sizes."""
-    return Nvfp4Group(a or None, b or None, sfa or None, sfb or None, c or None, m, n, k, reserved)
+    return Nvfp4Group(a or None, b or None, sfa or None, sfb or None, c or None, m, n, k, flags)
 
 
 def _array(groups: Sequence[Nvfp4Group]):
@@ -132,6 +138,31 @@ def stream_errors(stream: int = 0) -> int:
     return rc
 
 
+def swizzled_scale_bytes(rows: int, k: int) -> int:
+    """Bytes of the window-major layout of a [rows][k/16] scale matrix."""
+    return int(lib().nvfp4_swizzled_scale_bytes(rows, k))
+
+
+def swizzle_scales(sf, rows: int = None, k: int = None, stream=None):
+    """Window-major copy of a [rows, k/16] device tensor of scale bytes (a new
+    uint8 device tensor of swizzled_scale_bytes(rows, k) bytes), for use as
+    sfb with NVFP4_SFB_SWIZZLED.  Enqueued on `stream` (default: current)."""
+    import torch
+    if rows is None:
+        rows, kb = sf.shape
+        k = 16 * kb
+    if sf.numel() and (not sf.is_cuda or not sf.is_contiguous() or sf.element_size() != 1):
+        raise ValueError("sf must be a contiguous device tensor of bytes")
+    out = torch.empty(max(1, swizzled_scale_bytes(rows, k)), dtype=torch.uint8, device=sf.device)
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    rc = lib().nvfp4_swizzle_scales(ctypes.c_void_p(sf.data_ptr() or None), ctypes.c_void_p(out.data_ptr()),
+                                     rows, k, ctypes.c_void_p(stream.cuda_stream or None))
+    if rc != NVFP4_OK:
+        raise Nvfp4Error(rc, _last_error())
+    return out
+
+
 def tile_rows() -> int:
     return lib().nvfp4_tile_rows()
 
@@ -140,14 +171,17 @@ def tile_cols() -> int:
     return lib().nvfp4_tile_cols()
 
 
-def _descriptor(a, b, sfa, sfb, c) -> Nvfp4Group:
+def _descriptor(a, b, sfa, sfb, c, sfb_swizzled=False) -> Nvfp4Group:
     import torch
     m, kb = a.shape
     n = b.shape[0]
     k = 2 * kb
+    sfb_shape = (swizzled_scale_bytes(n, k),) if sfb_swizzled else (n, k // 16)
     for name, t, shape, dt in (("a", a, (m, kb), torch.uint8), ("b", b, (n, kb), torch.uint8),
-                               ("sfa", sfa, (m, k // 16), None), ("sfb", sfb, (n, k // 16), None),
+                               ("sfa", sfa, (m, k // 16), None), ("sfb", sfb, sfb_shape, None),
                                ("c", c, (m, n), torch.float16)):
+        if name == "sfb" and sfb_swizzled and t.numel() >= shape[0]:
+            shape = tuple(t.shape)    # the swizzled buffer may be larger
         if tuple(t.shape) != shape:
             raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), shape))
         if dt is not None and t.dtype != dt:
@@ -158,7 +192,8 @@ def _descriptor(a, b, sfa, sfb, c) -> Nvfp4Group:
             raise ValueError("%s must be contiguous" % name)
         if t.numel() and not t.is_cuda:
             raise ValueError("%s must be a device tensor" % name)
-    return make_group(a.data_ptr(), b.data_ptr(), sfa.data_ptr(), sfb.data_ptr(), c.data_ptr(), m, n, k)
+    return make_group(a.data_ptr(), b.data_ptr(), sfa.data_ptr(), sfb.data_ptr(), c.data_ptr(), m, n, k,
+                      NVFP4_SFB_SWIZZLED if sfb_swizzled else 0)
 
 
 def group_gemm(groups: Iterable, stream=None) -> None:
@@ -166,8 +201,9 @@ def group_gemm(groups: Iterable, stream=None) -> None:
 
     a: uint8 [M, K/2], b: uint8 [N, K/2] (packed E2M1, low nibble = even k),
     sfa: [M, K/16], sfb: [N, K/16] (E4M3FN bytes, uint8 or float8_e4m3fn),
-    c: float16 [M, N], written in place.  Runs on `stream` (a torch stream,
-    default: the current stream) without synchronising.
+    c: float16 [M, N], written in place.  A sixth element True marks sfb as
+    the window-major copy made by swizzle_scales.  Runs on `stream` (a torch
+    stream, default: the current stream) without synchronising.
     """
     import torch
     descs = [_descriptor(*g) for g in groups]

@@ -102,10 +102,31 @@ struct GroupArgs {
     int32_t npairs;      // stage pairs along K (>= 1)
     int32_t cost_full;   // cost of one pair of a tile with tile_rows rows
     int32_t cost_last;   // cost of one pair of the last row tile
-    int32_t pad_;
+    int32_t flags;       // NVFP4_SFB_SWIZZLED: sfb in the window-major layout
     int64_t strip_cost;  // cost of one column strip (all row tiles with heads)
     int64_t cost_begin;  // cost before this group's first tile
 };
+
+// The window-major scale layout (NVFP4_SFB_SWIZZLED): for each block of 32
+// rows and each 256-k window, the 16 scale bytes of the window of the 32
+// rows are contiguous, row after row (512 bytes), windows of one row block
+// after each other, row blocks after each other.  Rows are padded to a
+// multiple of 32 by repeating the last row and K to a multiple of 256 with
+// zero bytes.  Byte (row, b) of the plain [rows][k/16] matrix (b = scale
+// block along k) sits at swz_offset(row, b).  A wave's 32 columns then
+// fetch a window's scales as one contiguous 512-byte run.
+__host__ __device__ inline uint32_t swz_windows(int k)
+{
+    return (uint32_t)(k + 255) / 256u;
+}
+__host__ __device__ inline uint32_t swz_offset(uint32_t row, uint32_t b, uint32_t windows)
+{
+    return ((row >> 5) * windows + (b >> 4)) * 512u + (row & 31u) * 16u + (b & 15u);
+}
+__host__ __device__ inline uint64_t swz_bytes(int rows, int k)
+{
+    return (uint64_t)((rows + 31) / 32) * 32u * swz_windows(k) * 16u;
+}
 
 // Where one workgroup's range starts: its logical index w (workgroups are
 // dealt round-robin to the XCDs, and consecutive logical ranges share A rows
@@ -483,7 +504,9 @@ __device__ __forceinline__ void segment(const GroupArgs &G, uint32_t *err, int s
     const i32x4 ra_codes = rsrc(G.a, (uint32_t)M * row_bytes);
     const i32x4 ra_scales = rsrc(G.sfa, (uint32_t)M * row_scales);
     const i32x4 rb_codes = rsrc(G.b, (uint32_t)N * row_bytes);
-    const i32x4 rb_scales = rsrc(G.sfb, (uint32_t)N * row_scales);
+    const bool sfb_swz = (G.flags & NVFP4_SFB_SWIZZLED) != 0;
+    const uint32_t swz_w = swz_windows(K);
+    const i32x4 rb_scales = rsrc(G.sfb, sfb_swz ? (uint32_t)swz_bytes(N, K) : (uint32_t)N * row_scales);
 
     // A decode role: wave w decodes row block w % NRB (all four MFMA steps).
     // For NRB < W several waves decode the same block and store identical
@@ -497,7 +520,12 @@ __device__ __forceinline__ void segment(const GroupArgs &G, uint32_t *err, int s
     uint32_t b_voff[2], sb_voff[2];
     // B scale rows for one 32-lane load: lane 16 cb + r fetches column block
     // cb's row r (lanes 32..63 are masked off)
-    const uint32_t sb_voff32 = (uint32_t)min(n0 + 32 * wave + 16 * (q & 1) + r, N - 1) * row_scales;
+    // (window-major layout: the wave's 32 columns are one 32-row block, so
+    // lane l's 16 bytes are at 16 l of the window's 512-byte run)
+    const uint32_t sb_voff32 = sfb_swz ? 16u * (uint32_t)(16 * (q & 1) + r)
+                                       : (uint32_t)min(n0 + 32 * wave + 16 * (q & 1) + r, N - 1) * row_scales;
+    const uint32_t sb_base = sfb_swz ? (uint32_t)((n0 + 32 * wave) >> 5) * swz_w * 512u : 0u;
+    const uint32_t sb_stride = sfb_swz ? 512u : 16u;
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
         const uint32_t col = (uint32_t)min(n0 + 32 * wave + 16 * cb + r, N - 1);
@@ -532,10 +560,11 @@ __device__ __forceinline__ void segment(const GroupArgs &G, uint32_t *err, int s
     // Scale window w (stages 2w and 2w + 1: 16 bytes of each row) into window
     // buffer w % 2, fetched by lanes 0..15 (row r = lane).
     auto fetch_scales = [&](int w) {
-        const uint32_t sk = (uint32_t)min(w, (nstages - 1) >> 1) * (2u * kStageK / 16u);
+        const uint32_t wc = (uint32_t)min(w, (nstages - 1) >> 1);
+        const uint32_t sk = wc * (2u * kStageK / 16u);
         const uint32_t win = smem_base + kLdsWindows + (uint32_t)(w & 1) * kWindow;
         dma16_lanes16(win + kWinAScales + wave * 256u, sa_voff, ra_scales, sk);
-        dma16_lanes32(win + kWinBScales + wave * 2 * 256u, sb_voff32, rb_scales, sk);
+        dma16_lanes32(win + kWinBScales + wave * 2 * 256u, sb_voff32, rb_scales, sb_base + wc * sb_stride);
     };
     auto raw_slot = [&](int c) -> const uint8_t * {
         return smem + kLdsAOps + (uint32_t)(c % kRing) * kRawStage;
@@ -958,7 +987,7 @@ __device__ __forceinline__ double readlane_f64(double x, int l)
 // for the out-of-line copy, which must fit in few registers.
 template <bool kCompact>
 __device__ __forceinline__ void store_exact(const uint8_t *a, const uint8_t *sfa, const uint8_t *b, const uint8_t *sfb,
-                                            _Float16 *c, int M, int N, int K, int lrow, int lcol, int n)
+                                            _Float16 *c, int M, int N, int K, int lrow, int lcol, int n, bool sfb_swz)
 {
     const int lane = lane_id();
     const int nb = K >> 4;
@@ -966,7 +995,9 @@ __device__ __forceinline__ void store_exact(const uint8_t *a, const uint8_t *sfa
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void *)a, 0, M * (int)row_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void *)b, 0, N * (int)row_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc((void *)sfa, 0, M * (int)row_sc, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc((void *)sfb, 0, N * (int)row_sc, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)sfb, 0, sfb_swz ? (int)swz_bytes(N, K) : N * (int)row_sc, 0x00020000);
+    const uint32_t swz_w = swz_windows(K);
     for (int base = 0; base < n; base += 8) {
         const int cnt = n - base < 8 ? n - base : 8;
         const int lg = cnt == 1 ? 6 : (cnt == 2 ? 5 : (cnt <= 4 ? 4 : 3));   // log2 of the lanes per output
@@ -995,7 +1026,8 @@ __device__ __forceinline__ void store_exact(const uint8_t *a, const uint8_t *sfa
                 cb[buf][t][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, ob, 0, 0));
                 cb[buf][t][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, ob + 16u, 0, 0));
                 sa[buf][t] = __builtin_amdgcn_raw_buffer_load_b32(rsa, row * row_sc + bo, 0, 0);
-                sb[buf][t] = __builtin_amdgcn_raw_buffer_load_b32(rsb, col * row_sc + bo, 0, 0);
+                sb[buf][t] = __builtin_amdgcn_raw_buffer_load_b32(
+                    rsb, sfb_swz ? swz_offset(col, bo, swz_w) : col * row_sc + bo, 0, 0);
             }
         };
         auto sum = [&](auto buf_t, int g) -> double {
@@ -1069,9 +1101,9 @@ __device__ __forceinline__ void store_exact(const uint8_t *a, const uint8_t *sfa
 // outputs of one wave at risk), one copy for every tile height.
 __device__ __noinline__ void store_exact_more(const uint8_t *a, const uint8_t *sfa, const uint8_t *b,
                                               const uint8_t *sfb, _Float16 *c, int M, int N, int K, int lrow,
-                                              int lcol, int n)
+                                              int lcol, int n, bool sfb_swz)
 {
-    store_exact<true>(a, sfa, b, sfb, c, M, N, K, lrow, lcol, n);
+    store_exact<true>(a, sfa, b, sfb, c, M, N, K, lrow, lcol, n, sfb_swz);
 }
 
 // Outputs one wave must recompute after its tile's store: entry p of the
@@ -1173,7 +1205,8 @@ __device__ __forceinline__ FixList fix_small_outputs(const GroupArgs &G, int m0,
                     first = FixList{lrow, lcol, 64};
                     full = true;
                 } else {
-                    store_exact_more(G.a, G.sfa, G.b, G.sfb, G.c, G.m, G.n, G.k, lrow, lcol, 64);
+                    store_exact_more(G.a, G.sfa, G.b, G.sfb, G.c, G.m, G.n, G.k, lrow, lcol, 64,
+                                     (G.flags & NVFP4_SFB_SWIZZLED) != 0);
                 }
                 n = 0;
             }
@@ -1182,7 +1215,7 @@ __device__ __forceinline__ FixList fix_small_outputs(const GroupArgs &G, int m0,
     if (!full)
         first = FixList{lrow, lcol, n};
     else if (n > 0)
-        store_exact_more(G.a, G.sfa, G.b, G.sfb, G.c, G.m, G.n, G.k, lrow, lcol, n);
+        store_exact_more(G.a, G.sfa, G.b, G.sfb, G.c, G.m, G.n, G.k, lrow, lcol, n, (G.flags & NVFP4_SFB_SWIZZLED) != 0);
     return first;
 }
 
@@ -1262,7 +1295,7 @@ __global__ __launch_bounds__(64 * W, 1) void nvfp4_group_gemm_kernel(const Launc
     // unwritten flag); no workgroup changes it before all have started
     uint32_t last = __hip_atomic_load(&args.control[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     asm volatile("" : "+s"(G.a), "+s"(G.b), "+s"(G.sfa), "+s"(G.sfb), "+s"(G.c), "+s"(G.m), "+s"(G.n), "+s"(G.k),
-                 "+s"(G.tile_rows), "+s"(G.npairs), "+s"(G.row_tiles), "+s"(G.cost_full), "+s"(G.cost_last),
+                 "+s"(G.tile_rows), "+s"(G.npairs), "+s"(G.row_tiles), "+s"(G.cost_full), "+s"(G.cost_last), "+s"(G.flags),
                  "+s"(G.strip_cost), "+s"(G.cost_begin), "+s"(lo), "+s"(hi), "+v"(last));
     last = (uint32_t)__builtin_amdgcn_readfirstlane((int)last);
     const uint32_t epoch = last + 1u == 0u ? 1u : last + 1u;
@@ -1284,7 +1317,8 @@ __global__ __launch_bounds__(64 * W, 1) void nvfp4_group_gemm_kernel(const Launc
         // the tile's outputs at risk of exceeding the tolerance, recomputed
         // exactly over its stored values (one copy for every tile height)
         if (fix.n > 0)
-            store_exact<false>(G.a, G.sfa, G.b, G.sfb, G.c, G.m, G.n, G.k, fix.lrow, fix.lcol, fix.n);
+            store_exact<false>(G.a, G.sfa, G.b, G.sfb, G.c, G.m, G.n, G.k, fix.lrow, fix.lcol, fix.n,
+                               (G.flags & NVFP4_SFB_SWIZZLED) != 0);
         if (pe < G.npairs)
             break;                 // the range ends inside this tile
         p = next_tile(args.g, args.ng, args.total_cost, p);
@@ -1352,8 +1386,11 @@ __device__ __forceinline__ FixList direct_task(const GroupArgs &G, int m0, int r
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void *)G.a, 0, M * (int)row_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc((void *)G.sfa, 0, M * (int)row_sc, 0x00020000);
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void *)G.b, 0, N * (int)row_bytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc((void *)G.sfb, 0, N * (int)row_sc, 0x00020000);
-    uint32_t a_off[NRB], sa_off[NRB], b_off[2], sb_off[2];
+    const bool sfb_swz = (G.flags & NVFP4_SFB_SWIZZLED) != 0;
+    const uint32_t swz_w = swz_windows(K);
+    const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)G.sfb, 0, sfb_swz ? (int)swz_bytes(N, K) : N * (int)row_sc, 0x00020000);
+    uint32_t a_off[NRB], sa_off[NRB], b_off[2], sb_col[2];
 #pragma unroll
     for (int i = 0; i < NRB; ++i) {
         const uint32_t row = (uint32_t)min(m0 + 16 * i + r, M - 1);
@@ -1364,8 +1401,12 @@ __device__ __forceinline__ FixList direct_task(const GroupArgs &G, int m0, int r
     for (int cb = 0; cb < 2; ++cb) {
         const uint32_t col = (uint32_t)min(n0 + 32 * wave + 16 * cb + r, N - 1);
         b_off[cb] = col * row_bytes + 16u * q;
-        sb_off[cb] = col * row_sc + 2u * q;
+        sb_col[cb] = col;
     }
+    // scale bytes (column col, blocks b and b + 1) in either layout
+    auto sb_at = [&](uint32_t col, uint32_t b) -> uint32_t {
+        return sfb_swz ? swz_offset(col, b, swz_w) : col * row_sc + b;
+    };
     const int nch = (K + kStageK - 1) / kStageK;    // <= 4
     // every chunk's loads first; chunks past K are not loaded
     u32x4 ac[4][NRB], bc[4][2];
@@ -1382,7 +1423,7 @@ __device__ __forceinline__ FixList direct_task(const GroupArgs &G, int m0, int r
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb) {
                 bc[c][cb] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, b_off[cb] + kb, 0, 0));
-                sb[c][cb] = __builtin_amdgcn_raw_buffer_load_b16(rsb, sb_off[cb] + ks, 0, 0);
+                sb[c][cb] = __builtin_amdgcn_raw_buffer_load_b16(rsb, sb_at(sb_col[cb], ks + 2u * q), 0, 0);
             }
         }
     }
@@ -1434,7 +1475,7 @@ __global__ __launch_bounds__(64 * kDirectWaves) void nvfp4_direct_kernel(const D
     GroupArgs G = args.g[t.g];
     int task_rows = args.task_rows;
     asm volatile("" : "+s"(G.a), "+s"(G.b), "+s"(G.sfa), "+s"(G.sfb), "+s"(G.c), "+s"(G.m), "+s"(G.n), "+s"(G.k),
-                 "+s"(task_rows));
+                 "+s"(G.flags), "+s"(task_rows));
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (t.n0 + 32 * wave >= G.n)
         return;                    // this wave's columns lie past the group (no barrier follows)
@@ -1447,7 +1488,35 @@ __global__ __launch_bounds__(64 * kDirectWaves) void nvfp4_direct_kernel(const D
     default: fix = direct_task<4>(G, t.m0, rows, t.n0, wave); break;
     }
     if (fix.n > 0)
-        store_exact<false>(G.a, G.sfa, G.b, G.sfb, G.c, G.m, G.n, G.k, fix.lrow, fix.lcol, fix.n);
+        store_exact<false>(G.a, G.sfa, G.b, G.sfb, G.c, G.m, G.n, G.k, fix.lrow, fix.lcol, fix.n,
+                           (G.flags & NVFP4_SFB_SWIZZLED) != 0);
+}
+
+// Window-major copy of a scale matrix (see swz_offset): thread t writes the
+// 16 bytes of one (row, window) entry of the output.
+__global__ __launch_bounds__(256) void nvfp4_swizzle_kernel(const uint8_t *sf, uint8_t *out, int rows, int k,
+                                                              uint32_t entries)
+{
+    const uint32_t e = blockIdx.x * 256u + threadIdx.x;
+    if (e >= entries)
+        return;
+    const uint32_t windows = swz_windows(k);
+    const uint32_t row = ((e >> 5) / windows) * 32u + (e & 31u);     // entry order = output order
+    const uint32_t w = (e >> 5) % windows;
+    const uint32_t src_row = row < (uint32_t)rows ? row : (uint32_t)rows - 1u;
+    const uint32_t nb = (uint32_t)k >> 4;
+    uint8_t v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const uint32_t b = 16u * w + (uint32_t)j;
+        v[j] = b < nb ? sf[(size_t)src_row * nb + b] : (uint8_t)0;
+    }
+    u32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        o[j] = (uint32_t)v[4 * j] | (uint32_t)v[4 * j + 1] << 8 | (uint32_t)v[4 * j + 2] << 16 |
+               (uint32_t)v[4 * j + 3] << 24;
+    *reinterpret_cast<u32x4 *>(out + (size_t)e * 16u) = o;
 }
 
 // ------------------------------------------------------------------ host --
@@ -1476,8 +1545,8 @@ int validate(const nvfp4_group_t *groups, int ng)
             return fail(NVFP4_EINVAL, "group %d: negative size (m=%d n=%d k=%d)", i, G.m, G.n, G.k);
         if (G.k % 16 != 0)
             return fail(NVFP4_EINVAL, "group %d: k=%d is not a multiple of 16", i, G.k);
-        if (G.reserved != 0)
-            return fail(NVFP4_EINVAL, "group %d: reserved field must be 0", i);
+        if ((G.flags & ~NVFP4_SFB_SWIZZLED) != 0)
+            return fail(NVFP4_EINVAL, "group %d: unknown flags 0x%x", i, (unsigned)G.flags);
         if (G.m == 0 || G.n == 0)
             continue;
         if (G.c == nullptr)
@@ -1498,6 +1567,12 @@ int validate(const nvfp4_group_t *groups, int ng)
         if (G.k > 0 && ((((uintptr_t)G.a | (uintptr_t)G.b) & 15u) != 0 ||
                         (((uintptr_t)G.sfa | (uintptr_t)G.sfb) & 3u) != 0))
             return fail(NVFP4_EUNSUPPORTED, "group %d: operand pointer misaligned", i);
+        if ((G.flags & NVFP4_SFB_SWIZZLED) != 0) {
+            if (G.k > 0 && ((uintptr_t)G.sfb & 15u) != 0)
+                return fail(NVFP4_EUNSUPPORTED, "group %d: window-major sfb is not 16-byte aligned", i);
+            if (swz_bytes(G.n, G.k) >= (1ull << 31))
+                return fail(NVFP4_EUNSUPPORTED, "group %d: window-major sfb reaches 2 GiB", i);
+        }
     }
     return NVFP4_OK;
 }
@@ -1530,6 +1605,7 @@ int pack_launch(const nvfp4_group_t *groups, int ng, int &next, LaunchArgs &args
         A.b = static_cast<const uint8_t *>(G.b);
         A.sfa = static_cast<const uint8_t *>(G.sfa);
         A.sfb = static_cast<const uint8_t *>(G.sfb);
+        A.flags = G.flags;
         A.c = static_cast<_Float16 *>(G.c);
         A.m = G.m;
         A.n = G.n;
@@ -1985,6 +2061,37 @@ int launch_all(const nvfp4_group_t *groups, int ng, hipStream_t st, bool use_sta
 }
 
 }  // namespace
+
+extern "C" int64_t nvfp4_swizzled_scale_bytes(int rows, int k)
+{
+    if (rows <= 0 || k <= 0)
+        return 0;
+    return (int64_t)swz_bytes(rows, k);
+}
+
+extern "C" int nvfp4_swizzle_scales(const void *sf, void *out, int rows, int k, void *stream)
+{
+    g_err[0] = '\0';
+    if (rows < 0 || k < 0 || k % 16 != 0)
+        return fail(NVFP4_EINVAL, "rows = %d, k = %d: negative, or k not a multiple of 16", rows, k);
+    if (rows == 0 || k == 0)
+        return NVFP4_OK;
+    if (sf == nullptr || out == nullptr)
+        return fail(NVFP4_EINVAL, "NULL scale pointer");
+    if (((uintptr_t)out & 15u) != 0)
+        return fail(NVFP4_EUNSUPPORTED, "out is not 16-byte aligned");
+    const uint64_t bytes = swz_bytes(rows, k);
+    if (bytes >= (1ull << 31))
+        return fail(NVFP4_EUNSUPPORTED, "the layout reaches 2 GiB");
+    const uint32_t entries = (uint32_t)(bytes / 16u);
+    hipLaunchKernelGGL(nvfp4_swizzle_kernel, dim3((entries + 255u) / 256u), dim3(256), 0,
+                       reinterpret_cast<hipStream_t>(stream), static_cast<const uint8_t *>(sf),
+                       static_cast<uint8_t *>(out), rows, k, entries);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return fail(NVFP4_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return NVFP4_OK;
+}
 
 extern "C" int nvfp4_validate(const nvfp4_group_t *groups, int ng)
 {

@@ -41,11 +41,14 @@ extern "C" {
  *   sfa  E4M3FN scales of A, [m][k/16] bytes, row-major, one per 16
  *        consecutive k.  4-byte aligned.
  *   sfb  E4M3FN scales of B, [n][k/16] bytes, row-major.  4-byte aligned.
+ *        With NVFP4_SFB_SWIZZLED in flags: the same scales in the
+ *        window-major layout nvfp4_swizzle_scales writes (16-byte aligned).
  *   c    output, [m][n] IEEE fp16, row-major; written, never read.
  *        4-byte aligned.  Must not overlap another group's c or any input.
  *   m, n, k  problem sizes; m == 0 or n == 0 makes the group a no-op (its
  *        pointers are not read), k == 0 writes +0 to every element of c (a, b,
  *        sfa and sfb may then be NULL).
+ *   flags  0, or NVFP4_SFB_SWIZZLED; other bits are invalid.
  */
 typedef struct nvfp4_group {
     const void *a;
@@ -56,8 +59,11 @@ typedef struct nvfp4_group {
     int32_t m;
     int32_t n;
     int32_t k;
-    int32_t reserved; /* must be 0 */
+    int32_t flags;
 } nvfp4_group_t;
+
+/* sfb holds the window-major layout (see nvfp4_swizzle_scales). */
+#define NVFP4_SFB_SWIZZLED 1
 
 /*
  * Enqueue the grouped GEMM on `stream` (a hipStream_t; NULL = the null
@@ -68,7 +74,7 @@ typedef struct nvfp4_group {
  *   NVFP4_EINVAL        ng < 0; groups == NULL with ng > 0; m, n or k < 0;
  *                       k % 16 != 0; c == NULL in a group with m, n > 0; a,
  *                       b, sfa or sfb == NULL in such a group with k > 0;
- *                       reserved != 0.
+ *                       flags with a bit other than NVFP4_SFB_SWIZZLED.
  *   NVFP4_EUNSUPPORTED  k % 64 != 0 (the kernel moves k in stages of 64); a
  *                       pointer that breaks the alignment stated above; m,
  *                       n times k/2 reaching 2 GiB; the stream is being
@@ -126,6 +132,30 @@ int nvfp4_group_gemm(const nvfp4_group_t *groups, int ng, void *stream);
  * returns NVFP4_EUNSUPPORTED (not on MI355X, whose 256 compute units all fit).
  */
 int nvfp4_group_gemm_noalloc(const nvfp4_group_t *groups, int ng, void *stream);
+
+/*
+ * Bytes of the window-major layout of a [rows][k/16] scale matrix:
+ * ceil(rows/32)*32 rows of ceil(k/256)*16 bytes.  0 for rows or k <= 0.
+ */
+int64_t nvfp4_swizzled_scale_bytes(int rows, int k);
+
+/*
+ * Enqueues on `stream` a copy of the plain row-major scale matrix `sf`
+ * ([rows][k/16] E4M3FN bytes, device memory) into `out` (device memory of
+ * nvfp4_swizzled_scale_bytes(rows, k) bytes, 16-byte aligned, not
+ * overlapping sf) in the window-major layout: for each block of 32 rows and
+ * each 256-k window, the window's 16 scale bytes of the 32 rows, row after
+ * row; windows of a row block consecutive, row blocks consecutive.  Rows
+ * past `rows` repeat the last row, bytes past k/16 are 0.  Meant for a
+ * weight operand's scales, reordered once and reused: with
+ * NVFP4_SFB_SWIZZLED a wave's 32 columns read a window's scales as one
+ * contiguous 512-byte run instead of 32 runs of 16 bytes at a stride of
+ * k/16.  Results are identical to the plain layout's.
+ * Errors: NVFP4_EINVAL (rows or k < 0, k % 16 != 0, NULL pointer with rows,
+ * k > 0), NVFP4_EUNSUPPORTED (misaligned out, or the layout reaching 2 GiB),
+ * NVFP4_EHIP.
+ */
+int nvfp4_swizzle_scales(const void *sf, void *out, int rows, int k, void *stream);
 
 /*
  * Host-only argument check: the same validation nvfp4_group_gemm performs,

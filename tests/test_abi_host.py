@@ -51,7 +51,10 @@ def G(m, n, k, **kw):
     ([G(4, 4, 64, c=0)], nv.NVFP4_EINVAL),
     ([G(4, 4, 64, a=0)], nv.NVFP4_EINVAL),
     ([G(4, 4, 64, sfb=0)], nv.NVFP4_EINVAL),
-    ([G(4, 4, 64, reserved=1)], nv.NVFP4_EINVAL),
+    ([G(4, 4, 64, flags=2)], nv.NVFP4_EINVAL),          # unknown flag
+    ([G(4, 4, 64, flags=nv.NVFP4_SFB_SWIZZLED)], nv.NVFP4_OK),
+    ([G(4, 4, 64, flags=nv.NVFP4_SFB_SWIZZLED, sfb=SB + 4)], nv.NVFP4_EUNSUPPORTED),  # window-major sfb: 16 B
+    ([G(4, 4, 64, sfb=SB + 4)], nv.NVFP4_OK),           # plain sfb: 4 B is enough
     ([G(0, 4, 64, a=0, b=0, c=0)], nv.NVFP4_OK),          # empty group: pointers unused
     ([G(4, 0, 64, c=0)], nv.NVFP4_OK),
     ([G(4, 4, 0, a=0, b=0, sfa=0, sfb=0)], nv.NVFP4_OK),  # k == 0 writes zeros
@@ -255,3 +258,21 @@ def test_plan_random_shapes(seed):
         for roles in by_wg.values():
             if 2 in roles:
                 assert 1 not in roles[roles.index(2):]
+
+
+def test_swizzled_scale_bytes():
+    """ceil(rows / 32) * 32 rows of ceil(k / 256) windows of 16 bytes."""
+    assert nv.swizzled_scale_bytes(1, 16) == 32 * 1 * 16
+    assert nv.swizzled_scale_bytes(32, 256) == 32 * 1 * 16
+    assert nv.swizzled_scale_bytes(33, 257 - 1 + 16) == 64 * 2 * 16
+    assert nv.swizzled_scale_bytes(4096, 7168) == 4096 * 28 * 16
+    assert nv.swizzled_scale_bytes(0, 64) == 0 and nv.swizzled_scale_bytes(8, 0) == 0
+
+
+def test_swizzle_scales_rejects_before_launch():
+    lib = nv.lib()
+    assert lib.nvfp4_swizzle_scales(None, None, -1, 64, None) == nv.NVFP4_EINVAL
+    assert lib.nvfp4_swizzle_scales(None, None, 4, 24, None) == nv.NVFP4_EINVAL
+    assert lib.nvfp4_swizzle_scales(None, None, 4, 64, None) == nv.NVFP4_EINVAL
+    assert lib.nvfp4_swizzle_scales(None, None, 0, 64, None) == nv.NVFP4_OK       # nothing to do
+    assert lib.nvfp4_swizzle_scales(0x10000, 0x20008, 4, 64, None) == nv.NVFP4_EUNSUPPORTED
