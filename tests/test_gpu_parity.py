@@ -124,6 +124,57 @@ def test_edge_cases():
     assert (got[-1] == 0).all()
 
 
+def _random_codes_fixed_scale(rng, shapes, scale_code):
+    groups = []
+    for m, n, k in shapes:
+        groups.append(group(m, n, k, a=rng.integers(0, 256, (m, k // 2), dtype=np.uint8),
+                            b=rng.integers(0, 256, (n, k // 2), dtype=np.uint8),
+                            sfa=np.full((m, k // 16), scale_code, np.uint8),
+                            sfb=np.full((n, k // 16), scale_code, np.uint8)))
+    return groups
+
+
+@pytest.mark.parametrize("path", [None, "main"])
+def test_overflow_to_infinity(path):
+    """Every scale 24 (E4M3FN 0x5C) on both sides: rms(C) is about 8e4, so
+    many outputs overflow fp16 to +-inf (round to nearest even past 65504)
+    while the rest are large finite values.  Infinities must match the
+    oracle's in sign, finite outputs its value within tolerance.  The
+    launch is small enough for the direct kernel; path "main" forces the
+    persistent one.  The non-finite error estimate sends every output of a
+    wave through the exact recomputation, more than one list of 64."""
+    rng = np.random.default_rng(11)
+    groups = _random_codes_fixed_scale(rng, [(40, 96, 256), (130, 200, 512)], 0x5C)
+    with forced_path(path):
+        got = check_full(groups, "overflow, path %s" % path)
+    r16, _ = oracle.group_gemm(groups)
+    for gb, rb in zip(got, r16):
+        ref = rb.view(np.float16)
+        n_inf = int(np.isinf(ref).sum())
+        assert 0.1 * ref.size < n_inf < 0.9 * ref.size, n_inf      # both kinds of output occur
+        assert not np.isnan(gb.view(np.float16)).any()
+
+
+def test_subnormal_scales_and_outputs_bitexact():
+    """Every scale the smallest E4M3FN subnormal, 2^-9 (0x01): each product
+    is a multiple of 2^-20 and every partial sum stays below 2^4, so fp32
+    accumulation is exact in any order, and the fp16 results (many of them
+    subnormal) must equal the oracle's correctly rounded values bit for bit."""
+    rng = np.random.default_rng(12)
+    groups = _random_codes_fixed_scale(rng, [(33, 70, 1024), (16, 48, 64)], 0x01)
+    got = check_full(groups, "subnormal scales", exact=True)
+    sub = sum(int(((np.abs(g.view(np.float16)) < 2.0 ** -14) & (g.view(np.float16) != 0)).sum()) for g in got)
+    assert sub > 100, sub
+
+
+def test_long_k_many_parts():
+    """K = 32768 (64 folds of 512 k) on one small tile: the tile's 128 stage
+    pairs spread over 128 workgroups, so its finalizer adds over a hundred
+    partial sums; and a second group of two row tiles with K = 16384."""
+    w = workloads.make_workload([(24, 80, 32768), (130, 64, 16384)], (-4, 2), 13, "long_k")
+    check_full(workloads.generate(w), "long K")
+
+
 def test_many_groups_multiple_launches():
     shapes = [(int(m), int(n), 64 * int(kk)) for m, n, kk in
               zip(np.arange(1, 41) * 3, 16 + np.arange(40) * 5, 1 + np.arange(40) % 5)]
