@@ -29,6 +29,14 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 //  4: kind 0 plus the exact FP4 -> fp16 decode of 24 code dwords' worth of
 //     pairs (one convert and one packed multiply per pair), the VALU work a
 //     decode-to-fp16 path issues beside those MFMAs
+//  5: the FP4-MFMA alternative with a register rescale: 8 x
+//     v_mfma_scale_f32_32x32x64_f8f6f4 on FP4 operands, each covering one
+//     16-element NVFP4 scale block (the other 48 k zero, since the
+//     instruction's own scales are powers of two per 32 k), its 32 x 32
+//     partial started from zero and added into the accumulator times the
+//     per-output scale product: 16 multiplies (row scale x column scale) and
+//     16 fused multiply-adds per lane.  Counted flops are the useful ones
+//     (16 k per instruction).
 template <int KIND>
 __global__ __launch_bounds__(512, 1) void probe(float *out, unsigned long long *times, int iters, uint32_t seed)
 {
@@ -48,6 +56,10 @@ __global__ __launch_bounds__(512, 1) void probe(float *out, unsigned long long *
     for (int i = 0; i < 6; ++i)
         codes[i] = seed * 2654435761u + lane * 97u + i;
     const f16x2 sc = {(_Float16)1.125f, (_Float16)1.125f};
+    float sa16[16];                // row scales of the lane's 16 outputs (kind 5)
+    for (int j = 0; j < 16; ++j)
+        sa16[j] = 0.5f + 0.0625f * (float)((lane + j + seed) & 15);
+    float sbv = 1.125f;            // the lane's column scale (kind 5)
     f32x16 acc32[8];
     f32x4 acc16[16];
     for (int i = 0; i < 8; ++i)
@@ -65,6 +77,17 @@ __global__ __launch_bounds__(512, 1) void probe(float *out, unsigned long long *
 #pragma unroll
             for (int i = 0; i < 16; ++i)
                 acc16[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i & 1], b[(i >> 1) & 1], acc16[i], 0, 0, 0);
+        } else if constexpr (KIND == 5) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                asm volatile("" : "+v"(xa));       // a new block of codes every MFMA
+                const f32x16 part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(xa, xb, f32x16{}, 4, 4, 0, 0x7f,
+                                                                                    0, 0x7f);
+                asm volatile("" : "+v"(sbv));     // a new column scale every block
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    acc32[i & 3][j] = __builtin_fmaf(part[j], sa16[j] * sbv, acc32[i & 3][j]);
+            }
         } else {
 #pragma unroll
             for (int i = 0; i < 8; ++i)
@@ -106,10 +129,11 @@ __global__ __launch_bounds__(512, 1) void probe(float *out, unsigned long long *
     }
 }
 
-constexpr double kFlopsPerIter[5] = {8.0 * 32 * 32 * 16 * 2, 16.0 * 16 * 16 * 32 * 2, 8.0 * 32 * 32 * 64 * 2,
-                                     8.0 * 32 * 32 * 64 * 2, 8.0 * 32 * 32 * 16 * 2};
-constexpr const char *kNames[5] = {"f16 32x32x16", "f16 16x16x32", "fp8 32x32x64 (scaled)", "fp4 32x32x64 (scaled)",
-                                   "f16 32x32x16 + fp4->f16 decode of 48 values per 8 MFMA"};
+constexpr double kFlopsPerIter[6] = {8.0 * 32 * 32 * 16 * 2, 16.0 * 16 * 16 * 32 * 2, 8.0 * 32 * 32 * 64 * 2,
+                                     8.0 * 32 * 32 * 64 * 2, 8.0 * 32 * 32 * 16 * 2, 8.0 * 32 * 32 * 16 * 2};
+constexpr const char *kNames[6] = {"f16 32x32x16", "f16 16x16x32", "fp8 32x32x64 (scaled)", "fp4 32x32x64 (scaled)",
+                                   "f16 32x32x16 + fp4->f16 decode of 48 values per 8 MFMA",
+                                   "fp4 32x32x64, one 16-k scale block per MFMA + register rescale (useful flops)"};
 
 template <int KIND>
 int run(int waves, int iters, int launches, double &tflops, double &ghz)
@@ -187,5 +211,9 @@ extern "C" int nvfp4_probe_mfma_rates(char *buf, int cap)
     emit(3, 4, tf, ghz);
     rc |= run<4>(4, it, launches, tf, ghz);
     emit(4, 4, tf, ghz);
+    rc |= run<5>(4, it / 2, launches, tf, ghz);
+    emit(5, 4, tf, ghz);
+    rc |= run<5>(8, it / 4, launches, tf, ghz);
+    emit(5, 8, tf, ghz);
     return rc;
 }
