@@ -98,6 +98,24 @@ def test_bitexact_unit_scales_full_shape(cfg):
     check_full(groups, "unit scales, %s" % w.name, exact=True)
 
 
+@pytest.mark.parametrize("cfg", [1, 4])
+def test_bitexact_power_of_two_scales_full_shape(cfg):
+    """Every scale drawn from {1/4, 1/2, 1} (E4M3FN 0x28, 0x30, 0x38), per
+    16-element block: each term is a multiple of 2^-6 (0.25 times the
+    smallest scale product 1/16), and every partial sum stays below
+    K * 36 <= 2^18, under 2^24 quanta, so fp32 accumulation is exact in any
+    order and every output must equal the oracle bit for bit, with the scale
+    path exercised block by block at the full workload shapes."""
+    w = workloads.CONFIGS[cfg]
+    src = workloads.generate(w)
+    rng = np.random.default_rng(30 + cfg)
+    codes = np.array([0x28, 0x30, 0x38], np.uint8)
+    groups = [group(g.m, g.n, g.k, a=g.a, b=g.b,
+                    sfa=codes[rng.integers(0, 3, g.sfa.shape)], sfb=codes[rng.integers(0, 3, g.sfb.shape)])
+              for g in src]
+    check_full(groups, "power-of-two scales, %s" % w.name, exact=True)
+
+
 def test_deterministic():
     groups = workloads.generate(workloads.make_workload([(100, 200, 1024), (7, 64, 4096)], (-8, 4), 3))
     log("gpu case: determinism")
