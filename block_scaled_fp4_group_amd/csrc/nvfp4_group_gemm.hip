@@ -37,6 +37,13 @@
 //    (heavy cancellation) can still carry more absolute error than the
 //    tolerance allows; each finished tile estimates that error from its own
 //    sums and recomputes the few outputs at risk exactly (fix_small_outputs).
+//  * Launches too small to fill the chip (every K <= 512, at most 64 units)
+//    run on nvfp4_direct_kernel instead: one wave per 16-64 rows x 32
+//    columns with its operands in registers, the same decode, MFMA chain,
+//    epilogue and exact fix-up, and no workspace.
+//  * B's scales may also come in a window-major layout (NVFP4_SFB_SWIZZLED,
+//    written once by nvfp4_swizzle_scales): a wave's 32 columns then read a
+//    256-k window's scales as one contiguous 512-byte run.
 #include <hip/hip_runtime.h>
 #include <stdarg.h>
 #include <stdint.h>
