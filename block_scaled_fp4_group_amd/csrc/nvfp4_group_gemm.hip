@@ -1374,7 +1374,8 @@ struct DirectArgs {
     GroupArgs g[kMaxGroupsPerLaunch];
     int32_t ntasks;
     int32_t task_rows;   // 16, 32 or 64
-    int32_t pad_[2];
+    int32_t ngroups;     // records in g (unused ones zeroed)
+    int32_t pad_;
     DirectTask task[kDirectMaxTasks];
 };
 
@@ -1476,13 +1477,24 @@ __device__ __forceinline__ FixList direct_task(const GroupArgs &G, int m0, int r
 
 __global__ __launch_bounds__(64 * kDirectWaves) void nvfp4_direct_kernel(const DirectArgs args)
 {
-    // two rounds of argument loads: the task, then its group's fields (all
-    // at once, pinned so the compiler cannot sink them to their uses)
-    const DirectTask t = args.task[blockIdx.x];
-    GroupArgs G = args.g[t.g];
-    int task_rows = args.task_rows;
-    asm volatile("" : "+s"(G.a), "+s"(G.b), "+s"(G.sfa), "+s"(G.sfb), "+s"(G.c), "+s"(G.m), "+s"(G.n), "+s"(G.k),
-                 "+s"(G.flags), "+s"(task_rows));
+    // One round of argument loads for launches of at most two groups: the
+    // task and both groups' fields at once (pinned, so the compiler cannot
+    // sink them to their uses), then a select; a second round, for the
+    // task's group, only with more groups.
+    DirectTask t = args.task[blockIdx.x];
+    int task_rows = args.task_rows, ng = args.ngroups;
+    GroupArgs G0 = args.g[0], G1 = args.g[1];
+    asm volatile("" : "+s"(t.g), "+s"(t.m0), "+s"(t.n0), "+s"(task_rows), "+s"(ng));
+    asm volatile("" : "+s"(G0.a), "+s"(G0.b), "+s"(G0.sfa), "+s"(G0.sfb), "+s"(G0.c), "+s"(G0.m), "+s"(G0.n),
+                 "+s"(G0.k), "+s"(G0.flags));
+    asm volatile("" : "+s"(G1.a), "+s"(G1.b), "+s"(G1.sfa), "+s"(G1.sfb), "+s"(G1.c), "+s"(G1.m), "+s"(G1.n),
+                 "+s"(G1.k), "+s"(G1.flags));
+    GroupArgs G = t.g == 0 ? G0 : G1;
+    if (ng > 2) {
+        G = args.g[t.g];
+        asm volatile("" : "+s"(G.a), "+s"(G.b), "+s"(G.sfa), "+s"(G.sfb), "+s"(G.c), "+s"(G.m), "+s"(G.n), "+s"(G.k),
+                     "+s"(G.flags));
+    }
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (t.n0 + 32 * wave >= G.n)
         return;                    // this wave's columns lie past the group (no barrier follows)
@@ -2003,6 +2015,7 @@ bool direct_tasks(const LaunchArgs &args, DirectArgs &d)
         memcpy(d.g, args.g, sizeof d.g);
         d.ntasks = n;
         d.task_rows = rows;
+        d.ngroups = args.ng;
         return true;
     }
     return false;
